@@ -1,0 +1,43 @@
+"""CPU float64 oracle for the diffusion-transformer attention hot path.
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path may import, call or
+execute this package: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it. It shares no code, constant
+table or helper with the HIP library under
+``diffusion_transformer_attention_flash_amd/``; the two meet only through
+the seeded inputs of ``workloads/``.
+
+What it computes, each written from the plain definition (numpy, float64):
+
+* ``attention``       -- non-causal multi-head scaled-dot-product attention,
+                         output O and natural-log LSE per query row
+                         (diffusers "Accelerate inference" guide, section
+                         "Scaled dot product attention").
+* ``merge``           -- combine of partial (O, LSE) pairs computed over
+                         disjoint K/V chunks, as each ring-attention rank
+                         does after it has seen every K/V block (diffusers
+                         "Context parallelism" guide, sections "Ring
+                         Attention" and "Ring Anything Attention").
+* ``residual_diff``   -- First Block Cache's relative residual difference,
+                         sum|a-b| / sum|b| (ParaAttention guide, section
+                         "First Block Cache").
+* ``e4m3_encode`` / ``e4m3_decode`` / ``quant_per_tensor`` /
+  ``attention_fp8``   -- per-tensor dynamic fp8 (OCP E4M3FN) quantisation
+                         and attention on the dequantised values with the
+                         probabilities quantised before the P.V product
+                         (ParaAttention guide, section "fp8 quantization").
+
+Every function is pinned by tests in ``tests/test_oracle_pins.py`` against
+mathematics it does not share code with (arbitrary-precision brute force,
+closed forms, invariants, a library float8 cast). None is "parity unpinned".
+"""
+
+from .attention import attention, merge, softmax_rows
+from .residual import residual_diff
+from .fp8 import (E4M3_MAX, e4m3_decode, e4m3_encode, quant_per_tensor,
+                  attention_fp8)
+
+__all__ = [
+    "attention", "merge", "softmax_rows", "residual_diff", "E4M3_MAX",
+    "e4m3_decode", "e4m3_encode", "quant_per_tensor", "attention_fp8",
+]

@@ -1,0 +1,117 @@
+"""Oracle: per-tensor dynamic fp8 (OCP E4M3FN) quantisation and fp8 attention.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``); never on the product
+path.
+
+ParaAttention guide, section "fp8 quantization": dynamic quantisation to fp8
+lets 8-bit matrix units run; the default granularity is one scale per tensor
+(per-row scales are the more accurate option where supported). The pages fix
+neither the fp8 encoding nor the P handling, so these readings are taken:
+
+* Format: OCP E4M3FN -- 1 sign bit, 4 exponent bits (bias 7), 3 mantissa
+  bits; exponent 0 is subnormal (m/8 * 2^-6); S.1111.111 is NaN; there is no
+  infinity; the largest finite magnitude is 448.
+* Per-tensor scale: s = amax|x| / 448 computed in float32 (s = 1 when
+  amax = 0); code = e4m3(x / s) with the division in float32 and the
+  rounding to E4M3 round-to-nearest-even, saturating at +-448.
+* Attention on the dequantised values x^ = e4m3_value(code) * s, with the
+  probabilities quantised before the P.V product: p = exp(s_ij - m_i) lies in
+  (0, 1]; P8 = e4m3(448 p) uses the full E4M3 range; O = (P8 . V^) / (448 l)
+  with l = sum_j p_ij taken from the unquantised p; LSE = m + ln l.
+"""
+
+import numpy as np
+
+E4M3_MAX = 448.0
+_E4M3_NAN = 0x7F
+
+
+def e4m3_decode(codes):
+    """Value of each E4M3FN byte as float64 (NaN for S.1111.111)."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    normal = (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0)
+    subnormal = (m / 8.0) * 2.0 ** -6
+    val = np.where(e == 0, subnormal, normal)
+    val = np.where((e == 0xF) & ((c & 0x7) == 0x7), np.nan, val)
+    return sign * val
+
+
+# The 127 finite non-negative magnitudes, in code order 0x00 .. 0x7E. Codes
+# are monotone in magnitude, so "nearest, ties to even mantissa" is "nearest,
+# ties to the even code" along this table.
+_MAGS = e4m3_decode(np.arange(0x7F, dtype=np.uint8))
+
+
+def e4m3_encode(x):
+    """Round each value to the nearest E4M3FN code (ties to even), saturating.
+
+    Magnitudes at or above 448 map to +-448; NaN maps to 0x7F; the sign bit
+    is kept for values that round to zero (-0.0 -> 0x80).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    hi = np.searchsorted(_MAGS, a, side="left")          # first mag >= a
+    hi_c = np.minimum(hi, 0x7E)
+    lo_c = np.maximum(hi_c - 1, 0)
+    d_hi = _MAGS[hi_c] - a
+    d_lo = a - _MAGS[lo_c]
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi_c % 2 == 0))
+    code = np.where(pick_hi, hi_c, lo_c)
+    code = np.where(a == _MAGS[hi_c], hi_c, code)        # exact hit
+    code = np.where(a >= E4M3_MAX, 0x7E, code)           # saturate
+    code = np.where(np.signbit(x), code | 0x80, code)
+    code = np.where(np.isnan(x), _E4M3_NAN, code)
+    return code.astype(np.uint8)
+
+
+def quant_per_tensor(x):
+    """Per-tensor dynamic quantisation of ``x`` to E4M3FN.
+
+    Returns (codes: uint8 array of x's shape, s: the float32 scale as a Python
+    float) with s = amax|x|/448 in float32 (1 if amax = 0) and
+    codes = e4m3(float32(x) / s), the division correctly rounded in float32.
+    """
+    if hasattr(x, "detach"):
+        import torch
+        x = x.detach().to("cpu").to(torch.float32).numpy()
+    x32 = np.asarray(x, dtype=np.float32)
+    amax = np.float32(np.abs(x32).max()) if x32.size else np.float32(0)
+    if amax == 0:
+        s = np.float32(1.0)
+    else:
+        s = np.float32(amax / np.float32(E4M3_MAX))
+    y = (x32 / s).astype(np.float32)
+    return e4m3_encode(y.astype(np.float64)), float(s)
+
+
+def attention_fp8(q8, k8, v8, descale, scale, rows=None):
+    """Attention on per-tensor E4M3 inputs with P quantised to E4M3 at x448.
+
+    q8: [B,H,Nq,D] uint8 codes, k8/v8: [B,H,Nkv,D] uint8 codes,
+    descale: (s_q, s_k, s_v), scale: logit multiplier, rows: optional query
+    rows. Returns (O, LSE) in float64, shapes as ``oracle.attention``.
+    """
+    q = e4m3_decode(np.asarray(q8)) * float(descale[0])
+    k = e4m3_decode(np.asarray(k8)) * float(descale[1])
+    v = e4m3_decode(np.asarray(v8)) * float(descale[2])
+    B, H, Nq, D = q.shape
+    if k.shape[2] < 1:
+        raise ValueError("Nkv must be >= 1")
+    if rows is not None:
+        q = q[:, :, np.asarray(rows, dtype=np.int64), :]
+    nq = q.shape[2]
+    o = np.empty((B, H, nq, D), dtype=np.float64)
+    lse = np.empty((B, H, nq), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            s = float(scale) * (q[b, h] @ k[b, h].T)
+            m = s.max(axis=1, keepdims=True)
+            p = np.exp(s - m)
+            l = p.sum(axis=1, keepdims=True)
+            p8 = e4m3_decode(e4m3_encode(E4M3_MAX * p))
+            o[b, h] = (p8 @ v[b, h]) / (E4M3_MAX * l)
+            lse[b, h] = m[:, 0] + np.log(l[:, 0])
+    return o, lse

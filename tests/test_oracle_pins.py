@@ -1,0 +1,401 @@
+"""Pins of the CPU oracle against what the mathematics fixes (no GPU).
+
+Each test checks the oracle against something it shares no code with:
+arbitrary-precision brute force of the naive formula (mpmath), closed forms,
+invariants of softmax attention, the log-sum-exp identity that makes the
+ring-attention combine exact, and torch's own float8_e4m3fn cast. Each one is
+chosen so that a plausible slip in the oracle (a dropped max shift, a
+transposed operand, a missing scale, a wrong LSE base, the wrong fp8 bias or
+rounding) fails at least one of them.
+"""
+
+import math
+
+import mpmath
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+RNG = np.random.default_rng(1234)
+
+
+# --------------------------------------------------------------------------
+# Z1: brute force in 50-digit arithmetic, naive formula (no max shift).
+# --------------------------------------------------------------------------
+
+def _mp_attention(q, k, v, scale):
+    mpmath.mp.dps = 50
+    nq, d = q.shape
+    nkv = k.shape[0]
+    o = np.zeros((nq, v.shape[1]))
+    lse = np.zeros(nq)
+    for i in range(nq):
+        ex = []
+        for j in range(nkv):
+            s = mpmath.mpf(0)
+            for t in range(d):
+                s += mpmath.mpf(float(q[i, t])) * mpmath.mpf(float(k[j, t]))
+            ex.append(mpmath.exp(mpmath.mpf(scale) * s))
+        z = mpmath.fsum(ex)
+        lse[i] = float(mpmath.log(z))
+        for c in range(v.shape[1]):
+            o[i, c] = float(mpmath.fsum(ex[j] * mpmath.mpf(float(v[j, c]))
+                                        for j in range(nkv)) / z)
+    return o, lse
+
+
+@pytest.mark.parametrize("nq,nkv,d", [(1, 1, 1), (3, 8, 4), (4, 5, 3), (2, 7, 2)])
+def test_z1_bruteforce_attention(nq, nkv, d):
+    q = RNG.standard_normal((1, 2, nq, d)) * 2.0
+    k = RNG.standard_normal((1, 2, nkv, d))
+    v = RNG.standard_normal((1, 2, nkv, d + 1))
+    scale = 0.7
+    o, lse = oracle.attention(q, k, v, scale)
+    for h in range(2):
+        o_ref, lse_ref = _mp_attention(q[0, h], k[0, h], v[0, h], scale)
+        np.testing.assert_allclose(o[0, h], o_ref, rtol=1e-13, atol=1e-14)
+        np.testing.assert_allclose(lse[0, h], lse_ref, rtol=1e-13, atol=1e-14)
+
+
+def test_z1_bruteforce_merge_and_rows():
+    q = RNG.standard_normal((1, 1, 3, 4))
+    k = RNG.standard_normal((1, 1, 8, 4))
+    v = RNG.standard_normal((1, 1, 8, 4))
+    cuts = [(0, 3), (3, 4), (4, 8)]
+    parts = [oracle.attention(q, k[:, :, a:b], v[:, :, a:b], 0.5) for a, b in cuts]
+    o, lse = oracle.merge(np.stack([p[0] for p in parts]),
+                          np.stack([p[1] for p in parts]))
+    o_ref, lse_ref = _mp_attention(q[0, 0], k[0, 0], v[0, 0], 0.5)
+    np.testing.assert_allclose(o[0, 0], o_ref, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(lse[0, 0], lse_ref, rtol=1e-13, atol=1e-14)
+    # evaluating a subset of rows is the same as slicing the full result
+    o2, lse2 = oracle.attention(q, k, v, 0.5, rows=[2, 0])
+    np.testing.assert_allclose(o2[0, 0], o_ref[[2, 0]], rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(lse2[0, 0], lse_ref[[2, 0]], rtol=1e-13)
+
+
+def test_z1_bruteforce_residual_diff():
+    a = RNG.standard_normal(57)
+    b = RNG.standard_normal(57)
+    mpmath.mp.dps = 50
+    num = mpmath.fsum(abs(mpmath.mpf(float(x)) - mpmath.mpf(float(y))) for x, y in zip(a, b))
+    den = mpmath.fsum(abs(mpmath.mpf(float(y))) for y in b)
+    assert oracle.residual_diff(a, b) == pytest.approx(float(num / den), rel=1e-14)
+
+
+# --------------------------------------------------------------------------
+# Z2 .. Z9: invariants and closed forms of softmax attention.
+# --------------------------------------------------------------------------
+
+def test_z2_softmax_rows_sum_to_one_and_identity_v():
+    n = 37
+    q = RNG.standard_normal((1, 1, 5, 8))
+    k = RNG.standard_normal((1, 1, n, 8))
+    v = np.eye(n)[None, None]                     # V = I  =>  O = P
+    o, _ = oracle.attention(q, k, v, 0.3)
+    np.testing.assert_allclose(o.sum(axis=-1), 1.0, rtol=0, atol=1e-14)
+    assert (o > 0).all()
+    p, _, _ = oracle.softmax_rows(0.3 * (q[0, 0] @ k[0, 0].T))
+    np.testing.assert_allclose(o[0, 0], p, rtol=1e-13, atol=1e-15)
+
+
+def test_z3_identical_keys_give_mean_v():
+    n, d, scale = 50, 16, 0.25
+    q = RNG.standard_normal((1, 2, 6, d))
+    krow = RNG.standard_normal(d)
+    k = np.broadcast_to(krow, (1, 2, n, d)).copy()
+    v = RNG.standard_normal((1, 2, n, d))
+    o, lse = oracle.attention(q, k, v, scale)
+    np.testing.assert_allclose(o, np.broadcast_to(v.mean(axis=2, keepdims=True), o.shape),
+                               rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(lse, scale * (q @ krow) + math.log(n), rtol=1e-13)
+
+
+def test_z4_constant_v():
+    q = RNG.standard_normal((1, 1, 7, 8))
+    k = RNG.standard_normal((1, 1, 33, 8))
+    v = np.full((1, 1, 33, 8), -1.375)
+    o, _ = oracle.attention(q, k, v, 1.0)
+    np.testing.assert_allclose(o, -1.375, rtol=1e-14)
+
+
+def test_z5_single_key():
+    q = RNG.standard_normal((1, 3, 4, 8))
+    k = RNG.standard_normal((1, 3, 1, 8))
+    v = RNG.standard_normal((1, 3, 1, 8))
+    o, lse = oracle.attention(q, k, v, 0.125)
+    np.testing.assert_allclose(o, np.broadcast_to(v, o.shape), rtol=1e-15)
+    np.testing.assert_allclose(lse, 0.125 * (q @ k[:, :, 0, :, None])[..., 0], rtol=1e-14)
+
+
+@pytest.mark.parametrize("zero_q", [True, False])
+def test_z6_uniform_attention(zero_q):
+    n = 29
+    q = np.zeros((1, 1, 3, 8)) if zero_q else RNG.standard_normal((1, 1, 3, 8))
+    k = RNG.standard_normal((1, 1, n, 8))
+    v = RNG.standard_normal((1, 1, n, 8))
+    o, lse = oracle.attention(q, k, v, 0.0 if not zero_q else 0.4)
+    np.testing.assert_allclose(o, np.broadcast_to(v.mean(axis=2, keepdims=True), o.shape),
+                               rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(lse, math.log(n), rtol=1e-14)
+
+
+def test_z7_shift_of_all_keys():
+    q = RNG.standard_normal((1, 1, 5, 8))
+    k = RNG.standard_normal((1, 1, 40, 8))
+    v = RNG.standard_normal((1, 1, 40, 8))
+    c = RNG.standard_normal(8)
+    o1, l1 = oracle.attention(q, k, v, 0.3)
+    o2, l2 = oracle.attention(q, k + c, v, 0.3)
+    np.testing.assert_allclose(o2, o1, rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(l2 - l1, 0.3 * (q @ c), rtol=1e-11, atol=1e-12)
+
+
+def test_z8_permutations():
+    q = RNG.standard_normal((1, 1, 9, 8))
+    k = RNG.standard_normal((1, 1, 40, 8))
+    v = RNG.standard_normal((1, 1, 40, 5))
+    o1, l1 = oracle.attention(q, k, v, 0.3)
+    pk = RNG.permutation(40)
+    o2, l2 = oracle.attention(q, k[:, :, pk], v[:, :, pk], 0.3)
+    np.testing.assert_allclose(o2, o1, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(l2, l1, rtol=1e-13)
+    pq = RNG.permutation(9)
+    o3, l3 = oracle.attention(q[:, :, pq], k, v, 0.3)
+    np.testing.assert_allclose(o3, o1[:, :, pq], rtol=1e-13)
+    np.testing.assert_allclose(l3, l1[:, :, pq], rtol=1e-13)
+
+
+def test_z9_affine_in_v():
+    q = RNG.standard_normal((1, 1, 6, 8))
+    k = RNG.standard_normal((1, 1, 21, 8))
+    v = RNG.standard_normal((1, 1, 21, 8))
+    o1, _ = oracle.attention(q, k, v, 0.5)
+    o2, _ = oracle.attention(q, k, 2.5 * v - 0.75, 0.5)
+    np.testing.assert_allclose(o2, 2.5 * o1 - 0.75, rtol=1e-12, atol=1e-13)
+
+
+def test_transposed_operand_is_caught():
+    # q.k^T with a non-square, non-symmetric setup: O rows must be a convex
+    # combination of V rows weighted by softmax over KEYS (axis of k).
+    q = np.array([[[[1.0, 0.0]]]])
+    k = np.array([[[[2.0, 0.0], [0.0, 0.0], [-2.0, 0.0]]]])
+    v = np.array([[[[1.0], [2.0], [3.0]]]])
+    o, lse = oracle.attention(q, k, v, 1.0)
+    w = np.exp([2.0, 0.0, -2.0])
+    assert o[0, 0, 0, 0] == pytest.approx((w @ [1.0, 2.0, 3.0]) / w.sum(), rel=1e-15)
+    assert lse[0, 0, 0] == pytest.approx(math.log(w.sum()), rel=1e-15)
+
+
+# --------------------------------------------------------------------------
+# Z10: the merge of chunked partials equals unchunked attention.
+# --------------------------------------------------------------------------
+
+def _chunked(q, k, v, scale, lens):
+    parts, start = [], 0
+    for n in lens:
+        parts.append(oracle.attention(q, k[:, :, start:start + n], v[:, :, start:start + n], scale))
+        start += n
+    return oracle.merge(np.stack([p[0] for p in parts]), np.stack([p[1] for p in parts]))
+
+
+def test_z10_tiny_config_four_chunks():
+    c = workloads.CONFIGS["tiny"]
+    q, k, v = workloads.workload_qkv("tiny")
+    o_ref, l_ref = oracle.attention(q, k, v, 1.0 / math.sqrt(c["D"]))
+    o, l = _chunked(q, k, v, 1.0 / math.sqrt(c["D"]), c["chunks"])
+    np.testing.assert_allclose(o, o_ref, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(l, l_ref, rtol=1e-13)
+
+
+@pytest.mark.parametrize("trial", range(3))
+def test_z10_random_partitions(trial):
+    n = 300
+    q = RNG.standard_normal((1, 2, 11, 16))
+    k = RNG.standard_normal((1, 2, n, 16))
+    v = RNG.standard_normal((1, 2, n, 16))
+    cuts = np.sort(RNG.choice(np.arange(1, n), size=4 + trial, replace=False))
+    lens = np.diff(np.concatenate([[0], cuts, [n]])).tolist()
+    o_ref, l_ref = oracle.attention(q, k, v, 0.25)
+    o, l = _chunked(q, k, v, 0.25, lens)
+    np.testing.assert_allclose(o, o_ref, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(l, l_ref, rtol=1e-13)
+
+
+def test_z10_uneven_config_chunks_cover_sequence():
+    c = workloads.CONFIGS["flux_1024_chunked"]
+    lens = workloads.chunk_lengths(c["config"], c["N"], c["n_chunks"], c["min_chunk"])
+    assert len(lens) == 8 and sum(lens) == 4608 and min(lens) >= 64
+    assert len(set(lens)) > 1       # uneven
+    # the same partition on a small head count, fewer query rows
+    q, k, v = workloads.make_qkv(c["config"], 1, 1, 64, 4608, 128, qknorm=True)
+    o_ref, l_ref = oracle.attention(q, k, v, 128 ** -0.5)
+    o, l = _chunked(q, k, v, 128 ** -0.5, lens)
+    np.testing.assert_allclose(o, o_ref, rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(l, l_ref, rtol=1e-13)
+
+
+def test_merge_neg_inf_partials():
+    o_parts = RNG.standard_normal((3, 1, 1, 4, 8))
+    lse = RNG.standard_normal((3, 1, 1, 4))
+    lse[1, 0, 0, :] = -np.inf                          # chunk 1 saw nothing
+    lse[:, 0, 0, 2] = -np.inf                          # row 2: nothing at all
+    o, l = oracle.merge(o_parts, lse)
+    o_ref, l_ref = oracle.merge(o_parts[[0, 2]], lse[[0, 2]])
+    for r in (0, 1, 3):
+        np.testing.assert_allclose(o[0, 0, r], o_ref[0, 0, r], rtol=1e-14)
+        np.testing.assert_allclose(l[0, 0, r], l_ref[0, 0, r], rtol=1e-14)
+    assert np.all(o[0, 0, 2] == 0.0) and l[0, 0, 2] == -np.inf
+
+
+def test_merge_single_partial_is_identity():
+    o_parts = RNG.standard_normal((1, 2, 3, 4, 8))
+    lse = RNG.standard_normal((1, 2, 3, 4)) * 10
+    o, l = oracle.merge(o_parts, lse)
+    np.testing.assert_allclose(o, o_parts[0], rtol=1e-15)
+    np.testing.assert_allclose(l, lse[0], rtol=1e-15)
+
+
+# --------------------------------------------------------------------------
+# Z11: statistics of the workload recipe (scale 1/sqrt(D), QK-norm).
+# --------------------------------------------------------------------------
+
+def test_z11_workload_statistics():
+    # logits ~ N(0,1): E exp(s) = e^(1/2)  =>  LSE ~ ln N + 1/2
+    n = 4608
+    q, k, v = workloads.make_qkv(2, 1, 2, 512, n, 128, qknorm=True)
+    o, lse = oracle.attention(q, k, v, 128 ** -0.5)
+    assert abs(lse.mean() - (math.log(n) + 0.5)) < 0.02
+    # O ~ weighted mean of N(0,1) values: std ~ sqrt(sum p^2) ~ sqrt(e / N)
+    assert abs(o.std() / math.sqrt(math.e / n) - 1.0) < 0.1
+
+
+# --------------------------------------------------------------------------
+# Z12: residual_diff closed forms and the workload's expected value.
+# --------------------------------------------------------------------------
+
+def test_z12_residual_closed_forms():
+    b = RNG.standard_normal(1000)
+    assert oracle.residual_diff(b, b) == 0.0
+    assert oracle.residual_diff(2 * b, b) == pytest.approx(1.0, rel=1e-15)
+    assert oracle.residual_diff(np.zeros_like(b), b) == pytest.approx(1.0, rel=1e-15)
+    assert oracle.residual_diff(-b, b) == pytest.approx(2.0, rel=1e-15)
+    assert oracle.residual_diff(np.ones(4), np.zeros(4)) == math.inf
+    assert math.isnan(oracle.residual_diff(np.zeros(4), np.zeros(4)))
+    # argument order matters: the denominator is the previous step's |b|
+    assert oracle.residual_diff(b, 2 * b) == pytest.approx(0.5, rel=1e-15)
+
+
+def test_z12_residual_workload_value():
+    c = workloads.CONFIGS["flux_1024_fp8"]
+    a, b = workloads.residual_pair(c["config"], (1, 512, 3072), c["residual_noise"])
+    r = oracle.residual_diff(a, b)
+    # E|0.08 n| / E|b| = 0.08 for independent standard normals
+    assert abs(r - 0.08) < 0.002
+
+
+# --------------------------------------------------------------------------
+# Z13: the E4M3FN encoding against torch's float8_e4m3fn cast.
+# --------------------------------------------------------------------------
+
+def test_z13_decode_all_codes_match_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    mine = oracle.e4m3_decode(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(mine), nan) and nan.sum() == 2
+    np.testing.assert_array_equal(mine[~nan], ref[~nan])
+    assert mine[0x7E] == 448.0 and mine[0x01] == 2.0 ** -9 and mine[0x08] == 2.0 ** -6
+
+
+def test_z13_encode_matches_torch_in_range():
+    x = np.concatenate([
+        RNG.standard_normal(20000) * 30,                    # normal range
+        RNG.uniform(-2 ** -5, 2 ** -5, 5000),               # subnormals
+        oracle.e4m3_decode(np.arange(0x7E)) * np.where(RNG.random(0x7E) < 0.5, -1, 1),
+        # exact midpoints between neighbouring codes: ties to even
+        0.5 * (oracle.e4m3_decode(np.arange(0, 0x7D)) + oracle.e4m3_decode(np.arange(1, 0x7E))),
+        [448.0, -448.0, 0.0, -0.0, 2 ** -10, 3 * 2 ** -10],
+    ]).astype(np.float32)
+    mine = oracle.e4m3_encode(x.astype(np.float64))
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(mine, ref)
+
+
+def test_z13_encode_saturates():
+    x = np.array([448.0, 463.9, 464.0, 500.0, 1e30, -1e30, np.nan])
+    assert list(oracle.e4m3_encode(x)) == [0x7E, 0x7E, 0x7E, 0x7E, 0x7E, 0xFE, 0x7F]
+
+
+def test_z13_quant_per_tensor():
+    x = torch.randn(3, 5, 64, generator=torch.Generator().manual_seed(7)).to(torch.bfloat16)
+    codes, s = oracle.quant_per_tensor(x)
+    x32 = x.to(torch.float32)
+    amax = x32.abs().max()
+    assert s == pytest.approx(float(amax) / 448.0, rel=1e-7)
+    ref = (x32 / torch.tensor(s, dtype=torch.float32)).to(torch.float8_e4m3fn).view(torch.uint8)
+    np.testing.assert_array_equal(codes, ref.numpy())
+    # the absmax element lands on +-448 exactly
+    i = int(x32.abs().argmax())
+    assert codes.ravel()[i] & 0x7F == 0x7E
+    # relative error of in-range values is at most 2^-4 (3 mantissa bits)
+    xd = oracle.e4m3_decode(codes) * s
+    big = np.abs(x32.numpy()) >= s * 2 ** -6
+    rel = np.abs(xd - x32.numpy())[big] / np.abs(x32.numpy())[big]
+    assert rel.max() <= 2 ** -4 + 1e-7
+    codes0, s0 = oracle.quant_per_tensor(np.zeros(10, dtype=np.float32))
+    assert s0 == 1.0 and not codes0.any()
+
+
+# --------------------------------------------------------------------------
+# fp8 attention: closed forms and the P-rounding bound.
+# --------------------------------------------------------------------------
+
+def test_fp8_attention_identical_keys_exact():
+    # all logits equal -> p = 1 everywhere -> P8 = 448 exactly -> O = mean V^
+    d, n = 16, 24
+    q8 = oracle.e4m3_encode(RNG.standard_normal((1, 1, 4, d)) * 4)
+    k8 = np.broadcast_to(oracle.e4m3_encode(RNG.standard_normal(d) * 4), (1, 1, n, d)).copy()
+    v8 = oracle.e4m3_encode(RNG.standard_normal((1, 1, n, d)) * 4)
+    ds = (0.5, 0.25, 0.125)
+    o, lse = oracle.attention_fp8(q8, k8, v8, ds, 0.3)
+    v = oracle.e4m3_decode(v8) * 0.125
+    np.testing.assert_allclose(o[0, 0], np.broadcast_to(v[0, 0].mean(0), (4, d)), rtol=1e-14)
+    qd = oracle.e4m3_decode(q8) * 0.5
+    kd = oracle.e4m3_decode(k8[0, 0, 0]) * 0.25
+    np.testing.assert_allclose(lse[0, 0], 0.3 * (qd[0, 0] @ kd) + math.log(n), rtol=1e-13)
+
+
+def test_fp8_attention_exact_power_of_two_probabilities():
+    # logits 0, -ln2, -2 ln2 -> p in {1, 1/2, 1/4}; 448 p is exactly
+    # representable, so P quantisation is lossless and O has a closed form.
+    q8 = oracle.e4m3_encode(np.ones((1, 1, 1, 1)))
+    kv = np.array([0.0, -1.0, -2.0, -1.0, 0.0])
+    k8 = oracle.e4m3_encode(kv.reshape(1, 1, 5, 1))
+    vals = np.array([1.0, 2.0, 4.0, -3.0, 0.5])
+    v8 = oracle.e4m3_encode(vals.reshape(1, 1, 5, 1))
+    o, lse = oracle.attention_fp8(q8, k8, v8, (1.0, 1.0, 1.0), math.log(2.0))
+    p = 2.0 ** kv
+    assert o[0, 0, 0, 0] == pytest.approx((p @ vals) / p.sum(), rel=1e-14)
+    assert lse[0, 0, 0] == pytest.approx(math.log(p.sum()), rel=1e-14)
+
+
+def test_fp8_attention_close_to_dequantised_attention():
+    # Only P is rounded beyond the dequantised inputs: each 448 p is within
+    # 2^-4 relative (normal range) or 2^-10 absolute (subnormal range).
+    c = workloads.CONFIGS["flux_1024_fp8"]
+    q, k, v = workloads.make_qkv(c["config"], 1, 2, 64, 512, 128, qknorm=True)
+    (q8, sq), (k8, sk), (v8, sv) = (oracle.quant_per_tensor(t) for t in (q, k, v))
+    o8, l8 = oracle.attention_fp8(q8, k8, v8, (sq, sk, sv), 128 ** -0.5)
+    qd = oracle.e4m3_decode(q8) * sq
+    kd = oracle.e4m3_decode(k8) * sk
+    vd = oracle.e4m3_decode(v8) * sv
+    o, l = oracle.attention(qd, kd, vd, 128 ** -0.5)
+    np.testing.assert_allclose(l8, l, rtol=1e-14)
+    bound = (2 ** -4 + 512 * 2 ** -10 / 448.0 * 4) * np.abs(vd).max()
+    assert np.abs(o8 - o).max() <= bound
+    # and it is a genuine (if small) perturbation, not a no-op
+    assert np.abs(o8 - o).max() > 0
