@@ -1,0 +1,174 @@
+"""MI355X (gfx950) attention core of diffusion transformers.
+
+Thin binding over libdta.so (include/dta.h): each function checks dtypes,
+devices, shapes and contiguity, allocates outputs with torch if the caller
+did not pass them, and hands raw device pointers plus the current HIP stream
+to the C ABI. Every step of the computation runs in the library's HIP
+kernels; there is no fallback path -- a missing library raises.
+
+    attn_fwd(q, k, v, scale)              -> (o, lse)
+    attn_merge(o_parts, lse_parts)        -> (o, lse)
+    residual_diff(a, b)                   -> device float32 scalar
+    fp8_quant_per_tensor(x)               -> (x8 uint8, descale float32[1])
+    attn_fwd_fp8(q8, k8, v8, descale, scale) -> (o, lse)
+"""
+
+import torch
+
+from . import _lib
+from ._lib import DtaError  # noqa: F401
+
+__all__ = ["attn_fwd", "attn_merge", "residual_diff", "fp8_quant_per_tensor",
+           "attn_fwd_fp8", "workspace", "DtaError"]
+
+_workspaces = {}
+
+
+def _stream(t):
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _need(t, name, dtype, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be on a GPU, got %s" % (name, t.device))
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError("%s must have %d dims, got shape %s" % (name, ndim, tuple(t.shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _ptr(t):
+    return ctypes_ptr(t.data_ptr())
+
+
+def ctypes_ptr(addr):
+    import ctypes
+    return ctypes.c_void_p(addr)
+
+
+def workspace(device):
+    """The zero-filled reduction workspace of ``device`` (allocated once by torch)."""
+    device = torch.device(device)
+    idx = device.index if device.index is not None else torch.cuda.current_device()
+    ws = _workspaces.get(idx)
+    if ws is None:
+        nbytes = int(_lib.lib().dta_ws_bytes())
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device=torch.device("cuda", idx))
+        _workspaces[idx] = ws
+    return ws
+
+
+def attn_fwd(q, k, v, scale=None, o=None, lse=None):
+    """Non-causal attention: q [B,H,Nq,D], k/v [B,H,Nkv,D] bf16 -> (o bf16, lse f32)."""
+    _need(q, "q", torch.bfloat16, 4)
+    _need(k, "k", torch.bfloat16, 4)
+    _need(v, "v", torch.bfloat16, 4)
+    B, H, Nq, D = q.shape
+    Nkv = k.shape[2]
+    if tuple(k.shape) != (B, H, Nkv, D) or tuple(v.shape) != (B, H, Nkv, D):
+        raise ValueError("shape mismatch: q %s k %s v %s" % (tuple(q.shape), tuple(k.shape), tuple(v.shape)))
+    if scale is None:
+        scale = D ** -0.5
+    if o is None:
+        o = torch.empty_like(q)
+    else:
+        _need(o, "o", torch.bfloat16, 4)
+        if o.shape != q.shape:
+            raise ValueError("o must have q's shape")
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    else:
+        _need(lse, "lse", torch.float32, 3)
+        if tuple(lse.shape) != (B, H, Nq):
+            raise ValueError("lse must be [B,H,Nq]")
+    st = _lib.lib().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                             B, H, Nq, Nkv, D, float(scale), ctypes_ptr(_stream(q)))
+    _lib.check("attn_fwd", st)
+    return o, lse
+
+
+def attn_merge(o_parts, lse_parts, o=None, lse=None):
+    """Combine packed partials o_parts [n,B,H,Nq,D] bf16, lse_parts [n,B,H,Nq] f32."""
+    _need(o_parts, "o_parts", torch.bfloat16, 5)
+    _need(lse_parts, "lse_parts", torch.float32, 4)
+    n, B, H, Nq, D = o_parts.shape
+    if tuple(lse_parts.shape) != (n, B, H, Nq):
+        raise ValueError("lse_parts must be [n,B,H,Nq]")
+    if o is None:
+        o = torch.empty((B, H, Nq, D), dtype=torch.bfloat16, device=o_parts.device)
+    else:
+        _need(o, "o", torch.bfloat16, 4)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=o_parts.device)
+    else:
+        _need(lse, "lse", torch.float32, 3)
+    st = _lib.lib().attn_merge(_ptr(o_parts), _ptr(lse_parts), n, _ptr(o), _ptr(lse),
+                               B, H, Nq, D, ctypes_ptr(_stream(o_parts)))
+    _lib.check("attn_merge", st)
+    return o, lse
+
+
+def residual_diff(a, b, out=None):
+    """sum|a-b| / sum|b| over all elements of bf16 a, b -> float32 device scalar."""
+    _need(a, "a", torch.bfloat16)
+    _need(b, "b", torch.bfloat16)
+    if a.numel() != b.numel():
+        raise ValueError("a and b must have the same number of elements")
+    if out is None:
+        out = torch.empty((), dtype=torch.float32, device=a.device)
+    else:
+        _need(out, "out", torch.float32)
+    ws = workspace(a.device)
+    st = _lib.lib().residual_diff(_ptr(a), _ptr(b), a.numel(), _ptr(out), _ptr(ws),
+                                  ctypes_ptr(_stream(a)))
+    _lib.check("residual_diff", st)
+    return out
+
+
+def fp8_quant_per_tensor(x, x8=None, descale=None):
+    """Per-tensor E4M3FN quantisation of bf16 x -> (x8 uint8 codes, descale f32[1])."""
+    _need(x, "x", torch.bfloat16)
+    if x8 is None:
+        x8 = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    else:
+        _need(x8, "x8", torch.uint8)
+        if x8.numel() != x.numel():
+            raise ValueError("x8 must have x's element count")
+    if descale is None:
+        descale = torch.empty((1,), dtype=torch.float32, device=x.device)
+    else:
+        _need(descale, "descale", torch.float32)
+    ws = workspace(x.device)
+    st = _lib.lib().fp8_quant_per_tensor(_ptr(x), x.numel(), _ptr(x8), _ptr(descale),
+                                         _ptr(ws), ctypes_ptr(_stream(x)))
+    _lib.check("fp8_quant_per_tensor", st)
+    return x8, descale
+
+
+def attn_fwd_fp8(q8, k8, v8, descale, scale=None, o=None, lse=None):
+    """fp8 attention: E4M3FN codes (uint8) q8/k8/v8, descale f32[3] = (s_q, s_k, s_v)."""
+    _need(q8, "q8", torch.uint8, 4)
+    _need(k8, "k8", torch.uint8, 4)
+    _need(v8, "v8", torch.uint8, 4)
+    _need(descale, "descale", torch.float32)
+    if descale.numel() != 3:
+        raise ValueError("descale must hold 3 floats (s_q, s_k, s_v)")
+    B, H, Nq, D = q8.shape
+    Nkv = k8.shape[2]
+    if tuple(k8.shape) != (B, H, Nkv, D) or tuple(v8.shape) != (B, H, Nkv, D):
+        raise ValueError("shape mismatch")
+    if scale is None:
+        scale = D ** -0.5
+    if o is None:
+        o = torch.empty((B, H, Nq, D), dtype=torch.bfloat16, device=q8.device)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q8.device)
+    st = _lib.lib().attn_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(descale), _ptr(o),
+                                 _ptr(lse), B, H, Nq, Nkv, D, float(scale),
+                                 ctypes_ptr(_stream(q8)))
+    _lib.check("attn_fwd_fp8", st)
+    return o, lse

@@ -1,0 +1,109 @@
+// attn_merge: combine partial (O_p, LSE_p) over disjoint K/V chunks into the
+// attention over their union -- the exact log-sum-exp identity that lets a
+// ring-attention rank fold in each K/V block it receives (diffusers "Context
+// parallelism" guide, sections "Ring Attention" and "Ring Anything
+// Attention"):
+//     M = max_p LSE_p, w_p = exp(LSE_p - M), W = sum_p w_p,
+//     O = sum_p w_p O_p / W, LSE = M + ln W.
+//
+// HBM-bound scan. One thread owns 8 consecutive dims (16 bytes) of one row,
+// so every load and store is a coalesced 128-bit access; the per-row LSE
+// values are read by the D/8 threads of the row and served by one cache line.
+// Partials are visited four at a time so that several loads are in flight.
+
+#include "common.h"
+
+namespace dta {
+
+template <int D>
+__global__ __launch_bounds__(256) void attn_merge_kernel(
+    const uint16_t* __restrict__ op, const float* __restrict__ lp, int n,
+    uint16_t* __restrict__ o, float* __restrict__ lse, int64_t rows) {
+  constexpr int kCh = D / 8;
+  const int64_t total = rows * kCh;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t ci = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; ci < total;
+       ci += stride) {
+    const int64_t row = ci / kCh;
+    const int ch = (int)(ci - row * kCh);
+    float m = -INFINITY;
+    for (int p = 0; p < n; ++p) m = fmaxf(m, lp[(int64_t)p * rows + row]);
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float wsum = 0.f;
+    if (m != -INFINITY) {
+      const float ml2 = m * kLog2e;
+      int p = 0;
+      for (; p + 4 <= n; p += 4) {
+        u32x4 x[4];
+        float w[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          x[u] = *reinterpret_cast<const u32x4*>(
+              op + ((int64_t)(p + u) * rows + row) * D + ch * 8);
+          w[u] = __builtin_amdgcn_exp2f(
+              fmaf(lp[(int64_t)(p + u) * rows + row], kLog2e, -ml2));
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          wsum += w[u];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc[2 * e] = fmaf(w[u], bf16_bits_to_f32(x[u][e] & 0xFFFF), acc[2 * e]);
+            acc[2 * e + 1] = fmaf(w[u], bf16_bits_to_f32(x[u][e] >> 16), acc[2 * e + 1]);
+          }
+        }
+      }
+      for (; p < n; ++p) {
+        const u32x4 x = *reinterpret_cast<const u32x4*>(
+            op + ((int64_t)p * rows + row) * D + ch * 8);
+        const float w = __builtin_amdgcn_exp2f(
+            fmaf(lp[(int64_t)p * rows + row], kLog2e, -ml2));
+        wsum += w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[2 * e] = fmaf(w, bf16_bits_to_f32(x[e] & 0xFFFF), acc[2 * e]);
+          acc[2 * e + 1] = fmaf(w, bf16_bits_to_f32(x[e] >> 16), acc[2 * e + 1]);
+        }
+      }
+      const float inv = 1.0f / wsum;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] *= inv;
+    }
+    u32x4 out;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) out[e] = pack_bf16x2(acc[2 * e], acc[2 * e + 1]);
+    *reinterpret_cast<u32x4*>(o + row * D + ch * 8) = out;
+    if (ch == 0 && lse != nullptr)
+      lse[row] = (m == -INFINITY) ? -INFINITY : m + logf(wsum);
+  }
+}
+
+}  // namespace dta
+
+using namespace dta;
+
+extern "C" int attn_merge(const void* o_parts, const float* lse_parts,
+                          int n_parts, void* o, float* lse, int B, int H,
+                          int Nq, int D, hipStream_t stream) {
+  if (!o_parts || !lse_parts || !o) return DTA_EINVAL;
+  if (n_parts < 1 || B < 1 || H < 1 || Nq < 1) return DTA_EINVAL;
+  if (D != 64 && D != 128) return DTA_EUNSUPPORTED;
+  auto al = [](const void* p, uintptr_t a) {
+    return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0;
+  };
+  if (!al(o_parts, 16) || !al(o, 16) || !al(lse_parts, 4) || (lse && !al(lse, 4)))
+    return DTA_EALIGN;
+  const int64_t rows = (int64_t)B * H * Nq;
+  const int64_t total = rows * (D / 8);
+  const int64_t want = (total + 255) / 256;
+  const unsigned grid = (unsigned)(want < 65536 ? want : 65536);
+  if (D == 128)
+    hipLaunchKernelGGL(attn_merge_kernel<128>, dim3(grid), dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(o_parts), lse_parts, n_parts,
+                       static_cast<uint16_t*>(o), lse, rows);
+  else
+    hipLaunchKernelGGL(attn_merge_kernel<64>, dim3(grid), dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(o_parts), lse_parts, n_parts,
+                       static_cast<uint16_t*>(o), lse, rows);
+  return hipGetLastError() == hipSuccess ? DTA_OK : DTA_ELAUNCH;
+}

@@ -1,0 +1,264 @@
+// Grid-wide reductions over bf16 tensors:
+// * residual_diff -- First Block Cache's relative residual difference
+//   sum|a-b| / sum|b| (ParaAttention guide, section "First Block Cache").
+// * fp8_quant_per_tensor -- per-tensor dynamic E4M3FN quantisation, scale
+//   amax|x|/448 (ParaAttention guide, section "fp8 quantization").
+//
+// Both are HBM-bound scans. A fixed grid of kRedBlocks workgroups strides
+// over the tensor in 16-byte chunks (two chunks per thread per step, so that
+// four 128-bit loads are in flight), reduces in registers, then across the
+// wave and the workgroup. Each workgroup publishes one partial to the
+// workspace and takes a ticket; the last one to arrive sums the partials in
+// a fixed order in float64, writes the result and re-arms the ticket. The
+// result is therefore independent of scheduling and bitwise reproducible,
+// and the workspace is left zeroed for the next call.
+
+#include "common.h"
+
+namespace dta {
+
+struct RedWs {
+  unsigned int* ticket;  // kWsTicketBytes of counters
+  double* part;          // 2 * kRedBlocks partials
+};
+
+__device__ __forceinline__ RedWs red_ws(void* ws) {
+  char* base = static_cast<char*>(ws);
+  return {reinterpret_cast<unsigned int*>(base),
+          reinterpret_cast<double*>(base + kWsTicketBytes)};
+}
+
+// Workgroup-wide sum of two floats; valid in thread 0.
+__device__ __forceinline__ void block_sum2(float& x, float& y) {
+  __shared__ float sx[4], sy[4];
+  x = wave_sum(x);
+  y = wave_sum(y);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) {
+    sx[wave] = x;
+    sy[wave] = y;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    x = (sx[0] + sx[1]) + (sx[2] + sx[3]);
+    y = (sy[0] + sy[1]) + (sy[2] + sy[3]);
+  }
+}
+
+// Publishes this workgroup's partial and returns true in every thread of the
+// workgroup that arrives last. Release/acquire at device scope makes the
+// other workgroups' partials visible across XCDs.
+__device__ __forceinline__ bool arrive_last(unsigned int* ticket) {
+  __shared__ bool last;
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned int t = atomicAdd(ticket, 1u);
+    last = (t == gridDim.x - 1);
+  }
+  __syncthreads();
+  if (last) __threadfence();
+  return last;
+}
+
+__device__ __forceinline__ void abs_diff_acc(uint32_t a, uint32_t b, float& num,
+                                             float& den) {
+  const float a0 = bf16_bits_to_f32(a & 0xFFFF), a1 = bf16_bits_to_f32(a >> 16);
+  const float b0 = bf16_bits_to_f32(b & 0xFFFF), b1 = bf16_bits_to_f32(b >> 16);
+  num += fabsf(a0 - b0) + fabsf(a1 - b1);
+  den += fabsf(b0) + fabsf(b1);
+}
+
+__global__ __launch_bounds__(256) void residual_diff_kernel(
+    const uint16_t* __restrict__ a, const uint16_t* __restrict__ b, int64_t n,
+    float* __restrict__ out, void* ws) {
+  const RedWs w = red_ws(ws);
+  const int64_t n8 = n >> 3;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  const u32x4* a4 = reinterpret_cast<const u32x4*>(a);
+  const u32x4* b4 = reinterpret_cast<const u32x4*>(b);
+  float num = 0.f, den = 0.f;
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  for (; i + stride < n8; i += 2 * stride) {
+    const u32x4 xa0 = a4[i], xb0 = b4[i];
+    const u32x4 xa1 = a4[i + stride], xb1 = b4[i + stride];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) abs_diff_acc(xa0[e], xb0[e], num, den);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) abs_diff_acc(xa1[e], xb1[e], num, den);
+  }
+  if (i < n8) {
+    const u32x4 xa = a4[i], xb = b4[i];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) abs_diff_acc(xa[e], xb[e], num, den);
+  }
+  // Tail of fewer than 8 elements: the first threads of workgroup 0.
+  if (blockIdx.x == 0 && threadIdx.x < (n & 7)) {
+    const int64_t t = (n8 << 3) + threadIdx.x;
+    const float av = bf16_bits_to_f32(a[t]), bv = bf16_bits_to_f32(b[t]);
+    num += fabsf(av - bv);
+    den += fabsf(bv);
+  }
+  block_sum2(num, den);
+  if (threadIdx.x == 0) {
+    w.part[2 * blockIdx.x] = (double)num;
+    w.part[2 * blockIdx.x + 1] = (double)den;
+  }
+  if (!arrive_last(&w.ticket[kTicketResidual])) return;
+  // Fixed-order finish: thread t sums partials t, t+256, ... then a fixed tree.
+  __shared__ double fx[256], fy[256];
+  double x = 0.0, y = 0.0;
+  for (int p = threadIdx.x; p < (int)gridDim.x; p += 256) {
+    x += static_cast<volatile double*>(w.part)[2 * p];
+    y += static_cast<volatile double*>(w.part)[2 * p + 1];
+  }
+  fx[threadIdx.x] = x;
+  fy[threadIdx.x] = y;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (threadIdx.x < s) {
+      fx[threadIdx.x] += fx[threadIdx.x + s];
+      fy[threadIdx.x] += fy[threadIdx.x + s];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    *out = (float)(fx[0] / fy[0]);
+    w.ticket[kTicketResidual] = 0u;
+  }
+}
+
+// |x| maximum over bf16 bit patterns: for non-NaN values the order of the
+// sign-cleared 15-bit patterns is the order of the magnitudes.
+__device__ __forceinline__ uint32_t amax_bits(uint32_t w, uint32_t m) {
+  return max(m, max(w & 0x7FFFu, (w >> 16) & 0x7FFFu));
+}
+
+__global__ __launch_bounds__(256) void amax_kernel(
+    const uint16_t* __restrict__ x, int64_t n, float* __restrict__ descale,
+    void* ws) {
+  const RedWs w = red_ws(ws);
+  const int64_t n8 = n >> 3;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  const u32x4* x4 = reinterpret_cast<const u32x4*>(x);
+  uint32_t m = 0;
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  for (; i + stride < n8; i += 2 * stride) {
+    const u32x4 v0 = x4[i], v1 = x4[i + stride];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) m = amax_bits(v0[e], amax_bits(v1[e], m));
+  }
+  if (i < n8) {
+    const u32x4 v0 = x4[i];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) m = amax_bits(v0[e], m);
+  }
+  if (blockIdx.x == 0 && threadIdx.x < (n & 7))
+    m = max(m, (uint32_t)(x[(n8 << 3) + threadIdx.x] & 0x7FFFu));
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
+  __shared__ uint32_t sm[4];
+  if ((threadIdx.x & 63) == 0) sm[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t bm = max(max(sm[0], sm[1]), max(sm[2], sm[3]));
+    reinterpret_cast<uint32_t*>(w.part)[blockIdx.x] = bm;
+  }
+  if (!arrive_last(&w.ticket[kTicketAmax])) return;
+  uint32_t r = 0;
+  for (int p = threadIdx.x; p < (int)gridDim.x; p += 256)
+    r = max(r, reinterpret_cast<volatile uint32_t*>(w.part)[p]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) r = max(r, (uint32_t)__shfl_xor((int)r, off, 64));
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sm[threadIdx.x >> 6] = r;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t bm = max(max(sm[0], sm[1]), max(sm[2], sm[3]));
+    const float amax = bf16_bits_to_f32(bm);
+    *descale = (amax == 0.f) ? 1.0f : __fdiv_rn(amax, 448.0f);
+    w.ticket[kTicketAmax] = 0u;
+  }
+}
+
+// E4M3FN code of x / s: correctly rounded float32 division, clamp to the
+// finite range, then v_cvt_pk_fp8_f32 (round to nearest even).
+__device__ __forceinline__ float fp8_in(float x, float s) {
+  return fminf(fmaxf(__fdiv_rn(x, s), -448.0f), 448.0f);
+}
+
+__global__ __launch_bounds__(256) void fp8_cast_kernel(
+    const uint16_t* __restrict__ x, int64_t n, uint8_t* __restrict__ x8,
+    const float* __restrict__ descale) {
+  const float s = *descale;
+  const int64_t n8 = n >> 3;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  const u32x4* x4 = reinterpret_cast<const u32x4*>(x);
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += stride) {
+    const u32x4 v = x4[i];
+    u32x2 r;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t lo = v[2 * h], hi = v[2 * h + 1];
+      int wd = __builtin_amdgcn_cvt_pk_fp8_f32(
+          fp8_in(bf16_bits_to_f32(lo & 0xFFFF), s),
+          fp8_in(bf16_bits_to_f32(lo >> 16), s), 0, false);
+      wd = __builtin_amdgcn_cvt_pk_fp8_f32(
+          fp8_in(bf16_bits_to_f32(hi & 0xFFFF), s),
+          fp8_in(bf16_bits_to_f32(hi >> 16), s), wd, true);
+      r[h] = (uint32_t)wd;
+    }
+    *reinterpret_cast<u32x2*>(x8 + i * 8) = r;
+  }
+  if (blockIdx.x == 0 && threadIdx.x < (n & 7)) {
+    const int64_t t = (n8 << 3) + threadIdx.x;
+    const float y = fp8_in(bf16_bits_to_f32(x[t]), s);
+    x8[t] = (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(y, 0.f, 0, false) & 0xFF);
+  }
+}
+
+}  // namespace dta
+
+using namespace dta;
+
+static bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+extern "C" size_t dta_ws_bytes(void) { return kWsBytes; }
+
+extern "C" int residual_diff(const void* a, const void* b, int64_t n, float* out,
+                             void* ws, hipStream_t stream) {
+  if (!a || !b || !out || !ws || n < 1) return DTA_EINVAL;
+  if (!al16(a) || !al16(b) || !al16(ws) || (reinterpret_cast<uintptr_t>(out) & 3))
+    return DTA_EALIGN;
+  hipLaunchKernelGGL(residual_diff_kernel, dim3(kRedBlocks), dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(a), static_cast<const uint16_t*>(b),
+                     n, out, ws);
+  return hipGetLastError() == hipSuccess ? DTA_OK : DTA_ELAUNCH;
+}
+
+extern "C" int fp8_quant_per_tensor(const void* x, int64_t n, void* x8,
+                                    float* descale, void* ws, hipStream_t stream) {
+  if (!x || !x8 || !descale || !ws || n < 1) return DTA_EINVAL;
+  if (!al16(x) || !al16(x8) || !al16(ws) || (reinterpret_cast<uintptr_t>(descale) & 3))
+    return DTA_EALIGN;
+  hipLaunchKernelGGL(amax_kernel, dim3(kRedBlocks), dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(x), n, descale, ws);
+  if (hipGetLastError() != hipSuccess) return DTA_ELAUNCH;
+  const int64_t want = ((n >> 3) + 255) / 256;
+  const unsigned grid = (unsigned)(want < 1 ? 1 : (want < 8192 ? want : 8192));
+  hipLaunchKernelGGL(fp8_cast_kernel, dim3(grid), dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(x), n, static_cast<uint8_t*>(x8),
+                     descale);
+  return hipGetLastError() == hipSuccess ? DTA_OK : DTA_ELAUNCH;
+}
+
+extern "C" const char* dta_status_str(int status) {
+  switch (status) {
+    case DTA_OK: return "ok";
+    case DTA_EINVAL: return "invalid argument";
+    case DTA_EUNSUPPORTED: return "unsupported shape (head dim must be 64 or 128)";
+    case DTA_EALIGN: return "misaligned pointer";
+    case DTA_ELAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}

@@ -1,0 +1,143 @@
+/*
+ * dta.h -- C ABI of libdta.so, the MI355X (gfx950) diffusion-transformer
+ * attention core.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every tensor pointer is DEVICE memory owned by the caller. The library
+ *   never allocates, frees or synchronises; each call only enqueues kernels on
+ *   `stream` (0 = the null stream) and returns. Errors raised by the kernels
+ *   themselves surface at the caller's next synchronisation, as usual in HIP.
+ * - Layouts are dense row-major with 64-bit element offsets:
+ *   Q [B,H,Nq,D], K and V [B,H,Nkv,D], O [B,H,Nq,D], LSE [B,H,Nq].
+ * - Arguments are validated before any HIP call; a bad argument returns a
+ *   negative dta_status and enqueues nothing. Only DTA_ELAUNCH can follow a
+ *   HIP call. No function throws across the ABI.
+ * - bf16 means IEEE-style bfloat16 (1-8-7) stored as uint16; fp8 means OCP
+ *   E4M3FN bytes (bias 7, no infinities, max finite 448).
+ * - Nothing here is safe to run concurrently on two streams with the SAME
+ *   workspace `ws`.
+ */
+#ifndef DTA_H_
+#define DTA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DTA_OK = 0,
+  DTA_EINVAL = -1,        /* null pointer, non-positive size, bad scale      */
+  DTA_EUNSUPPORTED = -2,  /* a head dimension other than 64 or 128           */
+  DTA_EALIGN = -3,        /* a pointer not aligned as documented             */
+  DTA_ELAUNCH = -4        /* the HIP runtime refused the kernel launch       */
+} dta_status;
+
+/*
+ * attn_fwd -- non-causal multi-head scaled-dot-product attention, bf16 in,
+ * bf16 O and float32 natural-log LSE out.
+ *
+ * Defines (diffusers "Accelerate inference" guide, section "Scaled dot
+ * product attention"; no mask, no dropout, as the "Context parallelism"
+ * guide, section "Ring Anything Attention", requires):
+ *     s_ij = scale * q_i . k_j
+ *     O_i  = sum_j exp(s_ij) v_j / sum_j exp(s_ij)      (rounded to bf16)
+ *     LSE_i = ln sum_j exp(s_ij)                          (float32)
+ * Called on one contiguous K/V chunk it produces that chunk's partial
+ * (O, LSE), the local work of one ring-attention step (same guide, section
+ * "Ring Attention"); attn_merge then combines the partials.
+ *
+ * q        bf16 [B,H,Nq,D], 16-byte aligned
+ * k, v     bf16 [B,H,Nkv,D], 16-byte aligned
+ * o        bf16 [B,H,Nq,D], 16-byte aligned, written
+ * lse      float [B,H,Nq], 4-byte aligned, written (may be NULL: not written)
+ * B,H,Nq,Nkv >= 1; D in {64, 128}; scale finite and >= 0 (1/sqrt(D) is usual)
+ * Returns DTA_OK, DTA_EINVAL, DTA_EUNSUPPORTED, DTA_EALIGN or DTA_ELAUNCH.
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int B, int H, int Nq, int Nkv, int D, float scale,
+             hipStream_t stream);
+
+/*
+ * attn_merge -- combine partial (O_p, LSE_p), p = 0..n_parts-1, computed by
+ * attn_fwd over disjoint K/V chunks, into attention over their union:
+ *     M = max_p LSE_p;  w_p = exp(LSE_p - M);  W = sum_p w_p
+ *     O = sum_p w_p O_p / W  (bf16);  LSE = M + ln W  (float32)
+ * This is the exact log-sum-exp identity behind ring attention, where every
+ * rank has seen all tokens' K/V after a full turn (diffusers "Context
+ * parallelism" guide, sections "Ring Attention" and "Ring Anything
+ * Attention"). A partial with LSE = -inf gets zero weight; a row whose
+ * partials are all -inf gets O = 0 and LSE = -inf. Arithmetic is float32.
+ *
+ * o_parts   bf16 [n_parts,B,H,Nq,D] packed, 16-byte aligned
+ * lse_parts float [n_parts,B,H,Nq] packed, 4-byte aligned
+ * o         bf16 [B,H,Nq,D], 16-byte aligned, written (must not alias inputs)
+ * lse       float [B,H,Nq], written (may be NULL)
+ * n_parts >= 1; B,H,Nq >= 1; D in {64, 128}.
+ */
+int attn_merge(const void* o_parts, const float* lse_parts, int n_parts,
+               void* o, float* lse, int B, int H, int Nq, int D,
+               hipStream_t stream);
+
+/*
+ * residual_diff -- First Block Cache's relative residual difference
+ * (ParaAttention guide, section "First Block Cache"):
+ *     out = sum_k |a_k - b_k| / sum_k |b_k|  ( = mean|a-b| / mean|b| )
+ * over all n elements; a is the current step's first-block residual, b the
+ * previous step's. Per-thread float32 partial sums, a fixed-order float64
+ * finish, so the result is bitwise reproducible. sum|b| = 0 gives the IEEE
+ * quotient (+inf or NaN). The threshold compare stays with the caller.
+ *
+ * a, b  bf16 [n], 16-byte aligned; n >= 1
+ * out   float, one device scalar, written
+ * ws    device workspace of dta_ws_bytes() bytes, zero-filled by the caller
+ *       before its first use; every call leaves it zero-filled again.
+ */
+int residual_diff(const void* a, const void* b, int64_t n, float* out,
+                  void* ws, hipStream_t stream);
+
+/*
+ * fp8_quant_per_tensor -- per-tensor dynamic quantisation to E4M3FN
+ * (ParaAttention guide, section "fp8 quantization": one scale per tensor is
+ * the default granularity):
+ *     s = amax|x| / 448 in float32 (s = 1 if amax = 0)
+ *     x8 = e4m3_rne(float32(x) / s)   (correctly rounded float32 division,
+ *                                      round-to-nearest-even, saturating)
+ * x        bf16 [n], 16-byte aligned; n >= 1
+ * x8       uint8 [n], 16-byte aligned, written
+ * descale  float, one device scalar, written with s
+ * ws       as for residual_diff (may be the same buffer, not concurrently)
+ */
+int fp8_quant_per_tensor(const void* x, int64_t n, void* x8, float* descale,
+                         void* ws, hipStream_t stream);
+
+/*
+ * attn_fwd_fp8 -- the fp8 dynamic-quantisation variant of attn_fwd: Q, K, V
+ * are E4M3FN with per-tensor scales (as fp8_quant_per_tensor writes them);
+ * S = scale * s_q s_k (Q8 . K8^T) on fp8 MFMA with float32 accumulation;
+ * p = exp(s - m) is quantised to E4M3FN at x448 before the P.V product;
+ * O = (P8 . V8) s_v / (448 l) with l the float32 sum of the unquantised p;
+ * LSE = m + ln l. m is the running row maximum of the online softmax.
+ *
+ * q8, k8, v8  E4M3FN bytes, layouts as attn_fwd, 16-byte aligned
+ * descale     device float[3] = {s_q, s_k, s_v}
+ * o, lse      as attn_fwd. D in {64, 128}.
+ */
+int attn_fwd_fp8(const void* q8, const void* k8, const void* v8,
+                 const float* descale, void* o, float* lse, int B, int H,
+                 int Nq, int Nkv, int D, float scale, hipStream_t stream);
+
+/* Bytes of the workspace residual_diff and fp8_quant_per_tensor need. */
+size_t dta_ws_bytes(void);
+
+/* A static, human-readable name of a dta_status value. */
+const char* dta_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DTA_H_ */

@@ -1,0 +1,89 @@
+"""The C ABI: libdta.so loads, exports every symbol include/dta.h declares,
+and rejects bad arguments before any HIP call (runs without a GPU)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from diffusion_transformer_attention_flash_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dta.h")
+
+P = ctypes.c_void_p
+GOOD = ctypes.c_void_p(0x10000)          # 16-byte aligned, never dereferenced
+ODD = ctypes.c_void_p(0x10008)           # 8-byte aligned only
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_matches_binding_table():
+    assert declared_functions() == sorted(_lib.SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings_and_workspace_size():
+    lib = _lib.lib()
+    for s in (0, -1, -2, -3, -4, 99):
+        assert lib.dta_status_str(s)
+    assert lib.dta_ws_bytes() >= 256 + 16 * 1024
+
+
+def test_attn_fwd_validation():
+    f = _lib.lib().attn_fwd
+    ok = (GOOD, GOOD, GOOD, GOOD, GOOD)
+    assert f(None, GOOD, GOOD, GOOD, GOOD, 1, 1, 1, 1, 128, 0.1, None) == _lib.DTA_EINVAL
+    assert f(*ok, 0, 1, 1, 1, 128, 0.1, None) == _lib.DTA_EINVAL
+    assert f(*ok, 1, 1, 1, 0, 128, 0.1, None) == _lib.DTA_EINVAL       # empty K/V
+    assert f(*ok, 1, 1, 0, 1, 128, 0.1, None) == _lib.DTA_EINVAL
+    assert f(*ok, 1, 1, 1, 1, 96, 0.1, None) == _lib.DTA_EUNSUPPORTED
+    assert f(*ok, 1, 1, 1, 1, 128, -0.5, None) == _lib.DTA_EINVAL
+    assert f(*ok, 1, 1, 1, 1, 128, float("nan"), None) == _lib.DTA_EINVAL
+    assert f(*ok, 1, 1, 1, 1, 128, float("inf"), None) == _lib.DTA_EINVAL
+    assert f(ODD, GOOD, GOOD, GOOD, GOOD, 1, 1, 1, 1, 128, 0.1, None) == _lib.DTA_EALIGN
+    assert f(GOOD, GOOD, GOOD, GOOD, ctypes.c_void_p(0x10002), 1, 1, 1, 1, 64, 0.1, None) == _lib.DTA_EALIGN
+
+
+def test_attn_fwd_fp8_validation():
+    f = _lib.lib().attn_fwd_fp8
+    assert f(GOOD, GOOD, GOOD, None, GOOD, GOOD, 1, 1, 1, 1, 128, 0.1, None) == _lib.DTA_EINVAL
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 1, 1, 1, 1, 80, 0.1, None) == _lib.DTA_EUNSUPPORTED
+    assert f(GOOD, ODD, GOOD, GOOD, GOOD, GOOD, 1, 1, 1, 1, 64, 0.1, None) == _lib.DTA_EALIGN
+
+
+def test_attn_merge_validation():
+    f = _lib.lib().attn_merge
+    assert f(GOOD, GOOD, 0, GOOD, GOOD, 1, 1, 1, 128, None) == _lib.DTA_EINVAL
+    assert f(GOOD, None, 2, GOOD, GOOD, 1, 1, 1, 128, None) == _lib.DTA_EINVAL
+    assert f(GOOD, GOOD, 2, GOOD, GOOD, 1, 1, 1, 32, None) == _lib.DTA_EUNSUPPORTED
+    assert f(ODD, GOOD, 2, GOOD, GOOD, 1, 1, 1, 128, None) == _lib.DTA_EALIGN
+
+
+def test_reductions_validation():
+    lib = _lib.lib()
+    assert lib.residual_diff(GOOD, GOOD, 0, GOOD, GOOD, None) == _lib.DTA_EINVAL
+    assert lib.residual_diff(GOOD, GOOD, 10, GOOD, None, None) == _lib.DTA_EINVAL
+    assert lib.residual_diff(ODD, GOOD, 10, GOOD, GOOD, None) == _lib.DTA_EALIGN
+    assert lib.fp8_quant_per_tensor(GOOD, 0, GOOD, GOOD, GOOD, None) == _lib.DTA_EINVAL
+    assert lib.fp8_quant_per_tensor(GOOD, 10, ODD, GOOD, GOOD, None) == _lib.DTA_EALIGN
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    import diffusion_transformer_attention_flash_amd as dta
+    q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        dta.attn_fwd(q, q, q)
+    with pytest.raises(ValueError):
+        dta.residual_diff(q, q)

@@ -1,0 +1,76 @@
+"""GPU parity of the fp8 dynamic-quantisation attention variant."""
+
+import numpy as np
+import pytest
+import torch
+
+import diffusion_transformer_attention_flash_amd as dta
+import oracle
+import workloads
+from helpers import (FP8_O_MEAN_ABS, FP8_REL_L2_VS_BF16, FP8_REL_L2_VS_DEQUANT,
+                     LSE_ABS, rel_l2, to64)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _quant3(q, k, v):
+    q8, sq = dta.fp8_quant_per_tensor(q)
+    k8, sk = dta.fp8_quant_per_tensor(k)
+    v8, sv = dta.fp8_quant_per_tensor(v)
+    ds = torch.cat([sq, sk, sv])
+    return q8, k8, v8, ds
+
+
+def _check(o8, l8, q, k, v, q8, k8, v8, ds, scale, rows=None, what=""):
+    dsc = ds.cpu().tolist()
+    o_dq, l_dq = oracle.attention_fp8(q8.cpu().numpy(), k8.cpu().numpy(), v8.cpu().numpy(),
+                                      dsc, scale, rows=rows)
+    o_bf, l_bf = oracle.attention(q.cpu(), k.cpu(), v.cpu(), scale, rows=rows)
+    if rows is not None:
+        rt = torch.from_numpy(rows).to(o8.device)
+        o8, l8 = o8[:, :, rt], l8[:, :, rt]
+    o8, l8 = to64(o8), to64(l8)
+    assert np.isfinite(o8).all() and np.isfinite(l8).all()
+    mean_abs = np.abs(o8 - o_bf).mean()
+    r_bf = rel_l2(o8, o_bf)
+    r_dq = rel_l2(o8, o_dq)
+    e_l = np.abs(l8 - l_dq).max()
+    msg = "%s: O mean-abs %.3e vs bf16 oracle, rel-L2 %.3e (bf16) %.3e (dequant), LSE %.3e" % (
+        what, mean_abs, r_bf, r_dq, e_l)
+    print(msg)
+    assert mean_abs <= FP8_O_MEAN_ABS, msg
+    assert r_bf <= FP8_REL_L2_VS_BF16, msg
+    assert r_dq <= FP8_REL_L2_VS_DEQUANT, msg
+    assert e_l <= LSE_ABS, msg
+
+
+@pytest.mark.parametrize("B,H,Nq,Nkv,D", [(1, 2, 300, 300, 128), (1, 3, 200, 131, 64),
+                                          (1, 1, 64, 1, 128), (2, 1, 97, 640, 128)])
+def test_fp8_attention_shapes(B, H, Nq, Nkv, D):
+    print("CASE fp8 shape", B, H, Nq, Nkv, D, flush=True)
+    q, k, v = workloads.make_qkv(21, B, H, Nq, Nkv, D, device=DEV)
+    q8, k8, v8, ds = _quant3(q, k, v)
+    o8, l8 = dta.attn_fwd_fp8(q8, k8, v8, ds, D ** -0.5)
+    torch.cuda.synchronize()
+    _check(o8, l8, q, k, v, q8, k8, v8, ds, D ** -0.5, what="fp8 shape")
+
+
+def test_fp8_attention_peaked():
+    print("CASE fp8 peaked", flush=True)
+    q, k, v = workloads.make_qkv(23, 1, 2, 256, 512, 128, device=DEV, q_gain=4.0)
+    q8, k8, v8, ds = _quant3(q, k, v)
+    o8, l8 = dta.attn_fwd_fp8(q8, k8, v8, ds, 128 ** -0.5)
+    torch.cuda.synchronize()
+    _check(o8, l8, q, k, v, q8, k8, v8, ds, 128 ** -0.5, what="fp8 peaked")
+
+
+def test_fp8_flux_1024_sampled_rows():
+    c = workloads.CONFIGS["flux_1024_fp8"]
+    print("CASE fp8 flux_1024", flush=True)
+    q, k, v = workloads.workload_qkv("flux_1024_fp8", device=DEV)
+    q8, k8, v8, ds = _quant3(q, k, v)
+    o8, l8 = dta.attn_fwd_fp8(q8, k8, v8, ds, c["D"] ** -0.5)
+    torch.cuda.synchronize()
+    rows = workloads.sample_rows(c["config"], c["N"], 256, c["n_text"])
+    _check(o8, l8, q, k, v, q8, k8, v8, ds, c["D"] ** -0.5, rows=rows, what="fp8 flux")

@@ -1,0 +1,80 @@
+"""GPU parity of the chunked ring-step path: attn_fwd per K/V chunk + attn_merge."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import diffusion_transformer_attention_flash_amd as dta
+import oracle
+import workloads
+from helpers import assert_bf16_attention, to64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _chunked(q, k, v, scale, lens):
+    n = len(lens)
+    B, H, Nq, D = q.shape
+    o_parts = torch.empty((n, B, H, Nq, D), dtype=torch.bfloat16, device=q.device)
+    l_parts = torch.empty((n, B, H, Nq), dtype=torch.float32, device=q.device)
+    for i, (kc, vc) in enumerate(workloads.split_kv(k, v, lens)):
+        dta.attn_fwd(q, kc, vc, scale, o=o_parts[i], lse=l_parts[i])
+    o, lse = dta.attn_merge(o_parts, l_parts)
+    torch.cuda.synchronize()
+    return o, lse, o_parts, l_parts
+
+
+def test_tiny_four_chunks():
+    c = workloads.CONFIGS["tiny"]
+    print("CASE tiny 4x64 chunks", flush=True)
+    q, k, v = workloads.workload_qkv("tiny", device=DEV)
+    scale = 1.0 / math.sqrt(c["D"])
+    o, lse, _, _ = _chunked(q, k, v, scale, c["chunks"])
+    o_ref, lse_ref = oracle.attention(q.cpu(), k.cpu(), v.cpu(), scale)
+    assert_bf16_attention(o, lse, o_ref, lse_ref, "tiny chunked")
+    o1, l1 = dta.attn_fwd(q, k, v, scale)
+    torch.cuda.synchronize()
+    # chunked and unchunked agree to bf16 output rounding
+    assert np.abs(to64(o) - to64(o1)).max() < 2e-3
+
+
+def test_flux_eight_uneven_chunks():
+    c = workloads.CONFIGS["flux_1024_chunked"]
+    lens = workloads.chunk_lengths(c["config"], c["N"], c["n_chunks"], c["min_chunk"])
+    print("CASE flux_1024_chunked", lens, flush=True)
+    q, k, v = workloads.workload_qkv("flux_1024_chunked", device=DEV)
+    scale = c["D"] ** -0.5
+    o, lse, o_parts, l_parts = _chunked(q, k, v, scale, lens)
+    rows = workloads.sample_rows(c["config"], c["N"], 256, c["n_text"])
+    o_ref, lse_ref = oracle.attention(q.cpu(), k.cpu(), v.cpu(), scale, rows=rows)
+    rt = torch.from_numpy(rows).to(DEV)
+    assert_bf16_attention(o[:, :, rt], lse[:, :, rt], o_ref, lse_ref, "flux chunked")
+    # merge in isolation: the oracle's merge of the GPU's own partials
+    om, lm = oracle.merge(o_parts.cpu(), l_parts.cpu())
+    d_o = np.abs(to64(o) - om)
+    ulp = np.maximum(np.abs(om), 2.0 ** -126) * 2.0 ** -8     # one bf16 ulp (upper bound)
+    assert (d_o <= ulp + 1e-6).all(), "merge differs from oracle merge by > 1 bf16 ulp"
+    assert np.abs(to64(lse) - lm).max() < 1e-5
+
+
+@pytest.mark.parametrize("n_parts,D", [(1, 128), (3, 64), (5, 128), (9, 64)])
+def test_merge_random_partials(n_parts, D):
+    print("CASE merge n=%d D=%d" % (n_parts, D), flush=True)
+    g = torch.Generator().manual_seed(100 + n_parts)
+    B, H, Nq = 2, 3, 77
+    o_parts = torch.randn((n_parts, B, H, Nq, D), generator=g).to(torch.bfloat16)
+    l_parts = (torch.randn((n_parts, B, H, Nq), generator=g) * 5).to(torch.float32)
+    if n_parts > 2:
+        l_parts[1, 0, 0, :] = -math.inf            # a chunk that saw nothing
+        l_parts[:, 1, 2, 5] = -math.inf            # a row with nothing at all
+    o, lse = dta.attn_merge(o_parts.to(DEV), l_parts.to(DEV))
+    torch.cuda.synchronize()
+    om, lm = oracle.merge(o_parts, l_parts)
+    fin = np.isfinite(lm)
+    assert np.abs(to64(o) - om).max() < 2e-2
+    np.testing.assert_allclose(to64(lse)[fin], lm[fin], rtol=0, atol=1e-5)
+    assert (to64(lse)[~fin] == -np.inf).all()
+    assert (to64(o)[~fin] == 0).all()
