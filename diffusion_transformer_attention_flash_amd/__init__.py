@@ -51,7 +51,7 @@ def ctypes_ptr(addr):
 
 
 def workspace(device):
-    """The zero-filled reduction workspace of ``device`` (allocated once by torch)."""
+    """The reduction workspace of ``device`` (allocated once by torch)."""
     device = torch.device(device)
     idx = device.index if device.index is not None else torch.cuda.current_device()
     ws = _workspaces.get(idx)

@@ -7,26 +7,32 @@
 // attention"), evaluated by tiles with an online softmax, which rearranges
 // the same sums exactly.
 //
-// Design (one workgroup = NW waves = NW*QB*32 query rows of one (b, h)):
-// * The scores are computed transposed, S^T = K . Q^T, on
+// Design (one workgroup = NW waves = NW*32 query rows of one (b, h)):
+// * Scores are computed transposed, S^T = K . Q^T, on
 //   v_mfma_f32_32x32x16_bf16: K rows come from LDS as the A operand and the
-//   wave's Q rows sit in registers as the B operand for the whole K/V loop.
-//   In the 32x32 accumulator layout lane l then owns query l%32 and 16 of the
-//   32 keys (rows 8*(r/4) + 4*(l/32) + r%4 of register r), so the row max and
-//   row sum need only in-lane work plus one exchange between the two wave
-//   halves.
+//   wave's 32 Q rows stay in registers as the B operand for the whole K/V
+//   loop. In the 32x32 accumulator layout lane l then owns query l%32 and 16
+//   of every 32 keys (rows 8*(r/4) + 4*(l/32) + r%4 of register r), so the row
+//   max and row sum are in-lane work plus one v_permlane32_swap between the
+//   two wave halves.
 // * O is accumulated transposed too, O^T += V^T . P^T: the exponentiated
 //   scores, rounded to bf16, are the B operand straight from the registers
-//   that held S^T, and V^T comes from LDS. The contraction over keys only
-//   needs A and B to enumerate the same keys in the same (lane half, item)
-//   slots, so V^T is written to LDS with bits 2 and 3 of the key index
-//   swapped: the 8 keys a lane's P operand holds are then 8 consecutive
-//   bf16 of one V^T row (one 128-bit LDS read).
-// * K/V tiles (BN keys) are double-buffered in LDS; the next tile's global
-//   loads are issued before the current tile's MFMAs and land in the other
-//   buffer afterwards, so one barrier per tile suffices.
-// * Softmax runs in the log2 domain: c = scale*log2(e) is folded into one FMA
-//   per score before v_exp_f32. Only the last, partial tile masks keys.
+//   that held S^T. The V^T operand is read from the row-major V tile with
+//   ds_read_b64_tr_b16, whose 16-lane 4x4 transposes hand each lane 4 keys of
+//   one head dimension; two such reads cover exactly the 8 keys the lane's P
+//   operand holds, so no shuffle of P is needed.
+// * K and V tiles (BN keys) are double-buffered in LDS with XOR-swizzled
+//   16-byte chunks (conflict-free for the 128-bit K reads and the transposing
+//   V reads); the next tile's global loads are issued before the current
+//   tile's MFMAs and stored to the other buffer after them: one barrier per
+//   tile.
+// * Softmax runs in the log2 domain with c = scale*log2(e) folded into one FMA
+//   per score before v_exp_f32. The running max used for the exponent is only
+//   raised when some row's max grows by more than kTau (log2 units), so the
+//   O accumulator is rescaled rarely; p stays below 2^kTau, and O and l share
+//   the same reference max, so the result is exact.
+// * Only the last, partial K/V tile masks keys; its out-of-range rows are
+//   clamped loads of the last valid row, masked to zero weight.
 // * Workgroup ids are remapped so that the workgroups of one XCD walk
 //   consecutive query tiles of the same head and share K/V through its L2.
 
@@ -34,33 +40,58 @@
 
 namespace dta {
 
-template <int D, int NW, int QB, int BN>
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+template <int D, int NW, int BN>
 struct AttnCfg {
   static constexpr int kThreads = NW * 64;
-  static constexpr int kBM = NW * QB * 32;          // query rows per workgroup
-  static constexpr int kKS = D + 8;                 // K tile row stride (elements)
-  static constexpr int kVS = BN + 8;                // V^T tile row stride (elements)
-  static constexpr int kKElems = BN * kKS;
-  static constexpr int kVElems = D * kVS;
-  static constexpr int kChunks = BN * D / 8;        // 16-byte chunks per tile
+  static constexpr int kBM = NW * 32;               // query rows per workgroup
+  static constexpr int kCPR = D / 8;                // 16-byte chunks per row
+  static constexpr int kRP = 16 / kCPR;             // rows per 256 bytes
+  static constexpr int kTileElems = BN * D;
+  static constexpr int kChunks = BN * kCPR;         // chunks per tile
   static constexpr int kCpt = kChunks / kThreads;   // chunks per thread
   static_assert(kChunks % kThreads == 0, "tile must split evenly");
-  static_assert(BN % 32 == 0 && D % 32 == 0, "tile shape");
+  static_assert(BN % 32 == 0 && (D == 64 || D == 128), "tile shape");
 };
 
-// Position of key `key` (0..BN-1) inside a V^T row: bits 2 and 3 swapped.
-__device__ __forceinline__ int vt_pos(int key) {
-  return (key & ~0xC) | ((key & 4) << 1) | ((key & 8) >> 1);
+constexpr float kTau = 8.0f;
+
+// Physical 16-byte chunk of logical chunk `c` in row `r` of the K tile: the
+// 16 rows one 128-bit read wave-quarter touches land in distinct bank groups.
+template <int D>
+__device__ __forceinline__ int k_swz(int r, int c) {
+  constexpr int kCPR = D / 8, kRP = 16 / kCPR;
+  return c ^ ((r / kRP) % kCPR);
+}
+// Same for the V tile, read by ds_read_b64_tr_b16: 4 consecutive rows x 4
+// consecutive chunks per half-wave must hit distinct bank groups.
+template <int D>
+__device__ __forceinline__ int v_swz(int r, int c) {
+  constexpr int kCPR = D / 8, kRP = 16 / kCPR;
+  return c ^ (4 * ((r / kRP) % (kCPR / 4)));
 }
 
-template <int D, int NW, int QB, int BN>
-__global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(
+__device__ __forceinline__ float xhalf_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <int D, int NW, int BN>
+__global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
     float* __restrict__ lse, int Nq, int Nkv, float c, int n_qt) {
-  using C = AttnCfg<D, NW, QB, BN>;
-  __shared__ __attribute__((aligned(16))) uint16_t ks[2][C::kKElems];
-  __shared__ __attribute__((aligned(16))) uint16_t vts[2][C::kVElems];
+  using C = AttnCfg<D, NW, BN>;
+  __shared__ __attribute__((aligned(16))) uint16_t ks[2][C::kTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t vs[2][C::kTileElems];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -68,71 +99,58 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(
   const int blk = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = blk / n_qt, qt = blk - bh * n_qt;
   const int64_t q_base = (int64_t)bh * Nq * D;
-  const int64_t kv_base = (int64_t)bh * Nkv * D;
-  const int q0 = qt * C::kBM + wave * QB * 32;
+  const uint16_t* kh = k + (int64_t)bh * Nkv * D;
+  const uint16_t* vh = v + (int64_t)bh * Nkv * D;
+  const int row = qt * C::kBM + wave * 32 + l32;
 
-  // Q^T operand: query q0 + qb*32 + l32, dims ds*16 + 8g .. +7.
-  bf16x8 qr[QB][D / 16];
+  // Q^T operand: query `row`, dims ds*16 + 8g .. +7.
+  bf16x8 qr[D / 16];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int row = q0 + qb * 32 + l32;
-#pragma unroll
-    for (int ds = 0; ds < D / 16; ++ds) {
-      if (row < Nq) {
-        qr[qb][ds] = *reinterpret_cast<const bf16x8*>(
-            q + q_base + (int64_t)row * D + ds * 16 + g * 8);
-      } else {
-        qr[qb][ds] = bf16x8{};
-      }
-    }
-  }
+  for (int ds = 0; ds < D / 16; ++ds)
+    qr[ds] = (row < Nq) ? *reinterpret_cast<const bf16x8*>(q + q_base + (int64_t)row * D +
+                                                           ds * 16 + g * 8)
+                        : bf16x8{};
 
-  // K tile chunk mapping: 16 consecutive threads read one key row (coalesced).
-  // V tile chunk mapping: consecutive threads read consecutive keys, so the
-  // transposed 16-bit LDS writes of one wave fill one V^T row.
+  // Tile staging: chunk ci -> row ci / kCPR, logical chunk ci % kCPR; 16
+  // consecutive threads cover 256 contiguous bytes of global memory.
   u32x4 kreg[C::kCpt], vreg[C::kCpt];
   auto load_tile = [&](int j) {
     const int key0 = j * BN;
 #pragma unroll
     for (int it = 0; it < C::kCpt; ++it) {
       const int ci = it * C::kThreads + tid;
-      const int kk = ci / (D / 8), kd = ci % (D / 8);
-      const int vk = ci % BN, vd = ci / BN;
-      kreg[it] = (key0 + kk < Nkv)
-                     ? *reinterpret_cast<const u32x4*>(
-                           k + kv_base + (int64_t)(key0 + kk) * D + kd * 8)
-                     : u32x4{0, 0, 0, 0};
-      vreg[it] = (key0 + vk < Nkv)
-                     ? *reinterpret_cast<const u32x4*>(
-                           v + kv_base + (int64_t)(key0 + vk) * D + vd * 8)
-                     : u32x4{0, 0, 0, 0};
+      const int r = ci / C::kCPR, cc = ci % C::kCPR;
+      const int64_t gr = min(key0 + r, Nkv - 1);
+      kreg[it] = *reinterpret_cast<const u32x4*>(kh + gr * D + cc * 8);
+      vreg[it] = *reinterpret_cast<const u32x4*>(vh + gr * D + cc * 8);
     }
   };
   auto store_tile = [&](int buf) {
 #pragma unroll
     for (int it = 0; it < C::kCpt; ++it) {
       const int ci = it * C::kThreads + tid;
-      const int kk = ci / (D / 8), kd = ci % (D / 8);
-      const int vk = ci % BN, vd = ci / BN;
-      *reinterpret_cast<u32x4*>(&ks[buf][kk * C::kKS + kd * 8]) = kreg[it];
-      uint16_t* dst = &vts[buf][(vd * 8) * C::kVS + vt_pos(vk)];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        dst[(2 * e) * C::kVS] = (uint16_t)(vreg[it][e] & 0xFFFF);
-        dst[(2 * e + 1) * C::kVS] = (uint16_t)(vreg[it][e] >> 16);
-      }
+      const int r = ci / C::kCPR, cc = ci % C::kCPR;
+      *reinterpret_cast<u32x4*>(&ks[buf][r * D + k_swz<D>(r, cc) * 8]) = kreg[it];
+      *reinterpret_cast<u32x4*>(&vs[buf][r * D + v_swz<D>(r, cc) * 8]) = vreg[it];
     }
   };
 
-  f32x16 oacc[QB][D / 32];
-  float m_run[QB], l_run[QB];
+  // Per-lane constants of the operand reads.
+  int k_off[BN / 32][D / 16];            // element offset of the K A-operand chunk
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    m_run[qb] = -INFINITY;
-    l_run[qb] = 0.f;
+  for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) oacc[qb][db] = f32x16{};
-  }
+    for (int ds = 0; ds < D / 16; ++ds) {
+      const int r = kb * 32 + l32;
+      k_off[kb][ds] = r * D + k_swz<D>(r, 2 * ds + g) * 8;
+    }
+  const int vr_lo = 4 * g + ((lane & 15) >> 2);   // key offset inside 8-key group
+  const int vd_lo = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);  // dim offset in 32
+
+  f32x16 oacc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
 
   const int n_tiles = (Nkv + BN - 1) / BN;
   load_tile(0);
@@ -144,130 +162,118 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(
     const bool has_next = j + 1 < n_tiles;
     if (has_next) load_tile(j + 1);
     const uint16_t* kt = ks[buf];
-    const uint16_t* vt = vts[buf];
+    const uint16_t* vt = vs[buf];
 
-    // S^T = K . Q^T for BN keys x 32 queries per query block.
-    f32x16 s[QB][BN / 32];
+    // S^T = K . Q^T, BN keys x 32 queries.
+    f32x16 s[BN / 32];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
+    for (int kb = 0; kb < BN / 32; ++kb) s[kb] = f32x16{};
 #pragma unroll
-      for (int kb = 0; kb < BN / 32; ++kb) s[qb][kb] = f32x16{};
-#pragma unroll
-    for (int ds = 0; ds < D / 16; ++ds) {
+    for (int ds = 0; ds < D / 16; ++ds)
 #pragma unroll
       for (int kb = 0; kb < BN / 32; ++kb) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-            &kt[(kb * 32 + l32) * C::kKS + ds * 16 + g * 8]);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-          s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              a, qr[qb][ds], s[qb][kb], 0, 0, 0);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt + k_off[kb][ds]);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qr[ds], s[kb], 0, 0, 0);
       }
-    }
 
-    // Online softmax (log2 domain). Keys past Nkv exist only in the last tile.
+    // Online softmax in the log2 domain.
     const bool tail = (j + 1) * BN > Nkv;
     const int key_lim = Nkv - j * BN;
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      float mx = -INFINITY;
-      if (tail) {
-#pragma unroll
-        for (int kb = 0; kb < BN / 32; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-            if (key >= key_lim) s[qb][kb][r] = -INFINITY;
-          }
-      }
+    if (tail) {
 #pragma unroll
       for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qb][kb][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run[qb], mx * c);
-      const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new);
-      m_run[qb] = m_new;
-      float rs = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < BN / 32; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float p = __builtin_amdgcn_exp2f(fmaf(s[qb][kb][r], c, -m_new));
-          if (tail) {
-            const int key = kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-            if (key >= key_lim) p = 0.f;
-          }
-          s[qb][kb][r] = p;
-          rs += p;
-        }
-      l_run[qb] = l_run[qb] * alpha + rs;
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) oacc[qb][db] *= alpha;
+        for (int r = 0; r < 16; ++r)
+          if (kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3) >= key_lim) s[kb][r] = -INFINITY;
     }
-
-    // O^T += V^T . P^T, 16 keys per MFMA.
+    float mx = s[0][0];
 #pragma unroll
-    for (int kb = 0; kb < BN / 32; ++kb) {
+    for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    mx = xhalf_max(mx) * c;
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + kTau) != 0) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
+    }
+    float rs = 0.f;
+    bf16x8 pb[BN / 32][2];
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        bf16x8 pb[QB];
+        float p[8];
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          const f32x16& sv = s[qb][kb];
-          pb[qb] = bf16x8{(__bf16)sv[8 * t + 0], (__bf16)sv[8 * t + 1],
-                          (__bf16)sv[8 * t + 2], (__bf16)sv[8 * t + 3],
-                          (__bf16)sv[8 * t + 4], (__bf16)sv[8 * t + 5],
-                          (__bf16)sv[8 * t + 6], (__bf16)sv[8 * t + 7]};
+        for (int i = 0; i < 8; ++i) {
+          const int r = 8 * t + i;
+          p[i] = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c, -m_run));
+          if (tail && kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3) >= key_lim) p[i] = 0.f;
+          rs += p[i];
         }
+        pb[kb][t] = bf16x8{(__bf16)p[0], (__bf16)p[1], (__bf16)p[2], (__bf16)p[3],
+                           (__bf16)p[4], (__bf16)p[5], (__bf16)p[6], (__bf16)p[7]};
+      }
+    l_run += rs;
+
+    // O^T += V^T . P^T, 16 keys per MFMA; V^T via transposing LDS reads.
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-              &vt[(db * 32 + l32) * C::kVS + kb * 32 + 16 * t + 8 * g]);
+          s16x4 part[2];
 #pragma unroll
-          for (int qb = 0; qb < QB; ++qb)
-            oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                a, pb[qb], oacc[qb][db], 0, 0, 0);
+          for (int h = 0; h < 2; ++h) {
+            const int r = kb * 32 + 16 * t + 8 * h + vr_lo;
+            const int d = db * 32 + vd_lo;
+            const int off = r * D + v_swz<D>(r, d >> 3) * 8 + (d & 7);
+            part[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4*)(vt + off));
+          }
+          const s16x4 lo = part[0], hi = part[1];
+          const bf16x8 a = __builtin_bit_cast(
+              bf16x8, (short __attribute__((ext_vector_type(8)))){lo[0], lo[1], lo[2], lo[3],
+                                                                   hi[0], hi[1], hi[2], hi[3]});
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb][t], oacc[db], 0, 0, 0);
         }
-      }
-    }
 
     if (has_next) store_tile(buf ^ 1);
     __syncthreads();
   }
 
-  // Epilogue: lane owns query row (l32) and dims db*32 + 8*(r/4) + 4g + r%4.
+  // Epilogue: lane owns query `row` and dims db*32 + 8*(r/4) + 4g + r%4.
+  const float lt = xhalf_sum(l_run);
+  const float inv = 1.0f / lt;
+  if (row < Nq) {
+    uint16_t* orow = o + q_base + (int64_t)row * D;
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const float lt = l_run[qb] + __shfl_xor(l_run[qb], 32, 64);
-    const float inv = 1.0f / lt;
-    const int row = q0 + qb * 32 + l32;
-    if (row < Nq) {
-      uint16_t* orow = o + q_base + (int64_t)row * D;
+    for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const f32x16& a = oacc[qb][db];
-          u32x2 w = {pack_bf16x2(a[4 * jj] * inv, a[4 * jj + 1] * inv),
-                     pack_bf16x2(a[4 * jj + 2] * inv, a[4 * jj + 3] * inv)};
-          *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * jj + 4 * g) = w;
-        }
-      if (g == 0 && lse != nullptr)
-        lse[(int64_t)bh * Nq + row] = (m_run[qb] + log2f(lt)) * kLn2;
-    }
+      for (int jj = 0; jj < 4; ++jj) {
+        const f32x16& a = oacc[db];
+        u32x2 w = {pack_bf16x2(a[4 * jj] * inv, a[4 * jj + 1] * inv),
+                   pack_bf16x2(a[4 * jj + 2] * inv, a[4 * jj + 3] * inv)};
+        *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * jj + 4 * g) = w;
+      }
+    if (g == 0 && lse != nullptr)
+      lse[(int64_t)bh * Nq + row] = (m_run + log2f(lt)) * kLn2;
   }
 }
 
-template <int D, int NW, int QB, int BN>
+template <int D, int NW, int BN>
 static int launch_attn_fwd(const void* q, const void* k, const void* v,
                            void* o, float* lse, int B, int H, int Nq, int Nkv,
                            float scale, hipStream_t stream) {
-  using C = AttnCfg<D, NW, QB, BN>;
+  using C = AttnCfg<D, NW, BN>;
   const int n_qt = (Nq + C::kBM - 1) / C::kBM;
   const int64_t grid = (int64_t)n_qt * B * H;
   if (grid > 0x7FFFFFFF) return DTA_EUNSUPPORTED;
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, NW, QB, BN>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, NW, BN>), dim3((unsigned)grid),
                      dim3(C::kThreads), 0, stream,
                      static_cast<const uint16_t*>(q),
                      static_cast<const uint16_t*>(k),
@@ -295,6 +301,6 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o,
       (lse && !aligned(lse, 4)))
     return DTA_EALIGN;
   if (D == 128)
-    return launch_attn_fwd<128, 4, 1, 64>(q, k, v, o, lse, B, H, Nq, Nkv, scale, stream);
-  return launch_attn_fwd<64, 4, 1, 64>(q, k, v, o, lse, B, H, Nq, Nkv, scale, stream);
+    return launch_attn_fwd<128, 4, 64>(q, k, v, o, lse, B, H, Nq, Nkv, scale, stream);
+  return launch_attn_fwd<64, 4, 64>(q, k, v, o, lse, B, H, Nq, Nkv, scale, stream);
 }

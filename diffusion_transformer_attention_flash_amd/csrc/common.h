@@ -20,13 +20,10 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-// Workspace of the two grid-wide reductions: a ticket counter per reduction
-// kind followed by per-workgroup partials.
-constexpr int kRedBlocks = 1024;           // fixed grid of the reductions
-constexpr int kTicketResidual = 0;
-constexpr int kTicketAmax = 1;
-constexpr size_t kWsTicketBytes = 256;     // counters, padded to 256 B
-constexpr size_t kWsBytes = kWsTicketBytes + sizeof(double) * 2 * kRedBlocks;
+// Workspace of the two grid-wide reductions: one partial (two doubles) per
+// workgroup of their fixed grid.
+constexpr int kRedBlocks = 1024;
+constexpr size_t kWsBytes = sizeof(double) * 2 * kRedBlocks;
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);

@@ -7,26 +7,17 @@
 // Both are HBM-bound scans. A fixed grid of kRedBlocks workgroups strides
 // over the tensor in 16-byte chunks (two chunks per thread per step, so that
 // four 128-bit loads are in flight), reduces in registers, then across the
-// wave and the workgroup. Each workgroup publishes one partial to the
-// workspace and takes a ticket; the last one to arrive sums the partials in
-// a fixed order in float64, writes the result and re-arms the ticket. The
-// result is therefore independent of scheduling and bitwise reproducible,
-// and the workspace is left zeroed for the next call.
+// wave and the workgroup, and writes one partial per workgroup to the
+// workspace. A second, one-workgroup kernel combines the partials in a fixed
+// order in float64. The kernel boundary, not a device-scope fence, publishes
+// the partials: on gfx950 such a fence writes back the whole L2 of the XCD,
+// and one per workgroup costs more than the scan itself. The result is
+// independent of scheduling and bitwise reproducible, and the workspace needs
+// no initialisation.
 
 #include "common.h"
 
 namespace dta {
-
-struct RedWs {
-  unsigned int* ticket;  // kWsTicketBytes of counters
-  double* part;          // 2 * kRedBlocks partials
-};
-
-__device__ __forceinline__ RedWs red_ws(void* ws) {
-  char* base = static_cast<char*>(ws);
-  return {reinterpret_cast<unsigned int*>(base),
-          reinterpret_cast<double*>(base + kWsTicketBytes)};
-}
 
 // Workgroup-wide sum of two floats; valid in thread 0.
 __device__ __forceinline__ void block_sum2(float& x, float& y) {
@@ -45,22 +36,6 @@ __device__ __forceinline__ void block_sum2(float& x, float& y) {
   }
 }
 
-// Publishes this workgroup's partial and returns true in every thread of the
-// workgroup that arrives last. Release/acquire at device scope makes the
-// other workgroups' partials visible across XCDs.
-__device__ __forceinline__ bool arrive_last(unsigned int* ticket) {
-  __shared__ bool last;
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const unsigned int t = atomicAdd(ticket, 1u);
-    last = (t == gridDim.x - 1);
-  }
-  __syncthreads();
-  if (last) __threadfence();
-  return last;
-}
-
 __device__ __forceinline__ void abs_diff_acc(uint32_t a, uint32_t b, float& num,
                                              float& den) {
   const float a0 = bf16_bits_to_f32(a & 0xFFFF), a1 = bf16_bits_to_f32(a >> 16);
@@ -71,8 +46,7 @@ __device__ __forceinline__ void abs_diff_acc(uint32_t a, uint32_t b, float& num,
 
 __global__ __launch_bounds__(256) void residual_diff_kernel(
     const uint16_t* __restrict__ a, const uint16_t* __restrict__ b, int64_t n,
-    float* __restrict__ out, void* ws) {
-  const RedWs w = red_ws(ws);
+    double* __restrict__ part) {
   const int64_t n8 = n >> 3;
   const int64_t stride = (int64_t)gridDim.x * 256;
   const u32x4* a4 = reinterpret_cast<const u32x4*>(a);
@@ -101,16 +75,20 @@ __global__ __launch_bounds__(256) void residual_diff_kernel(
   }
   block_sum2(num, den);
   if (threadIdx.x == 0) {
-    w.part[2 * blockIdx.x] = (double)num;
-    w.part[2 * blockIdx.x + 1] = (double)den;
+    part[2 * blockIdx.x] = (double)num;
+    part[2 * blockIdx.x + 1] = (double)den;
   }
-  if (!arrive_last(&w.ticket[kTicketResidual])) return;
-  // Fixed-order finish: thread t sums partials t, t+256, ... then a fixed tree.
+}
+
+// One workgroup: fixed-order float64 sum of the kRedBlocks partial pairs --
+// thread t adds partials t, t+256, ..., then a fixed binary tree.
+__global__ __launch_bounds__(256) void residual_diff_finish_kernel(
+    const double* __restrict__ part, float* __restrict__ out) {
   __shared__ double fx[256], fy[256];
   double x = 0.0, y = 0.0;
-  for (int p = threadIdx.x; p < (int)gridDim.x; p += 256) {
-    x += static_cast<volatile double*>(w.part)[2 * p];
-    y += static_cast<volatile double*>(w.part)[2 * p + 1];
+  for (int p = threadIdx.x; p < kRedBlocks; p += 256) {
+    x += part[2 * p];
+    y += part[2 * p + 1];
   }
   fx[threadIdx.x] = x;
   fy[threadIdx.x] = y;
@@ -122,10 +100,7 @@ __global__ __launch_bounds__(256) void residual_diff_kernel(
     }
     __syncthreads();
   }
-  if (threadIdx.x == 0) {
-    *out = (float)(fx[0] / fy[0]);
-    w.ticket[kTicketResidual] = 0u;
-  }
+  if (threadIdx.x == 0) *out = (float)(fx[0] / fy[0]);
 }
 
 // |x| maximum over bf16 bit patterns: for non-NaN values the order of the
@@ -135,9 +110,7 @@ __device__ __forceinline__ uint32_t amax_bits(uint32_t w, uint32_t m) {
 }
 
 __global__ __launch_bounds__(256) void amax_kernel(
-    const uint16_t* __restrict__ x, int64_t n, float* __restrict__ descale,
-    void* ws) {
-  const RedWs w = red_ws(ws);
+    const uint16_t* __restrict__ x, int64_t n, uint32_t* __restrict__ part) {
   const int64_t n8 = n >> 3;
   const int64_t stride = (int64_t)gridDim.x * 256;
   const u32x4* x4 = reinterpret_cast<const u32x4*>(x);
@@ -162,22 +135,24 @@ __global__ __launch_bounds__(256) void amax_kernel(
   __syncthreads();
   if (threadIdx.x == 0) {
     const uint32_t bm = max(max(sm[0], sm[1]), max(sm[2], sm[3]));
-    reinterpret_cast<uint32_t*>(w.part)[blockIdx.x] = bm;
+    part[blockIdx.x] = bm;
   }
-  if (!arrive_last(&w.ticket[kTicketAmax])) return;
+}
+
+// One workgroup: maximum of the kRedBlocks partial maxima, then the scale.
+__global__ __launch_bounds__(256) void amax_finish_kernel(
+    const uint32_t* __restrict__ part, float* __restrict__ descale) {
+  __shared__ uint32_t sm[4];
   uint32_t r = 0;
-  for (int p = threadIdx.x; p < (int)gridDim.x; p += 256)
-    r = max(r, reinterpret_cast<volatile uint32_t*>(w.part)[p]);
+  for (int p = threadIdx.x; p < kRedBlocks; p += 256) r = max(r, part[p]);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) r = max(r, (uint32_t)__shfl_xor((int)r, off, 64));
-  __syncthreads();
   if ((threadIdx.x & 63) == 0) sm[threadIdx.x >> 6] = r;
   __syncthreads();
   if (threadIdx.x == 0) {
     const uint32_t bm = max(max(sm[0], sm[1]), max(sm[2], sm[3]));
     const float amax = bf16_bits_to_f32(bm);
     *descale = (amax == 0.f) ? 1.0f : __fdiv_rn(amax, 448.0f);
-    w.ticket[kTicketAmax] = 0u;
   }
 }
 
@@ -230,9 +205,12 @@ extern "C" int residual_diff(const void* a, const void* b, int64_t n, float* out
   if (!a || !b || !out || !ws || n < 1) return DTA_EINVAL;
   if (!al16(a) || !al16(b) || !al16(ws) || (reinterpret_cast<uintptr_t>(out) & 3))
     return DTA_EALIGN;
+  double* part = static_cast<double*>(ws);
   hipLaunchKernelGGL(residual_diff_kernel, dim3(kRedBlocks), dim3(256), 0, stream,
                      static_cast<const uint16_t*>(a), static_cast<const uint16_t*>(b),
-                     n, out, ws);
+                     n, part);
+  if (hipGetLastError() != hipSuccess) return DTA_ELAUNCH;
+  hipLaunchKernelGGL(residual_diff_finish_kernel, dim3(1), dim3(256), 0, stream, part, out);
   return hipGetLastError() == hipSuccess ? DTA_OK : DTA_ELAUNCH;
 }
 
@@ -241,8 +219,11 @@ extern "C" int fp8_quant_per_tensor(const void* x, int64_t n, void* x8,
   if (!x || !x8 || !descale || !ws || n < 1) return DTA_EINVAL;
   if (!al16(x) || !al16(x8) || !al16(ws) || (reinterpret_cast<uintptr_t>(descale) & 3))
     return DTA_EALIGN;
+  uint32_t* part = static_cast<uint32_t*>(ws);
   hipLaunchKernelGGL(amax_kernel, dim3(kRedBlocks), dim3(256), 0, stream,
-                     static_cast<const uint16_t*>(x), n, descale, ws);
+                     static_cast<const uint16_t*>(x), n, part);
+  if (hipGetLastError() != hipSuccess) return DTA_ELAUNCH;
+  hipLaunchKernelGGL(amax_finish_kernel, dim3(1), dim3(256), 0, stream, part, descale);
   if (hipGetLastError() != hipSuccess) return DTA_ELAUNCH;
   const int64_t want = ((n >> 3) + 255) / 256;
   const unsigned grid = (unsigned)(want < 1 ? 1 : (want < 8192 ? want : 8192));

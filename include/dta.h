@@ -15,8 +15,8 @@
  *   HIP call. No function throws across the ABI.
  * - bf16 means IEEE-style bfloat16 (1-8-7) stored as uint16; fp8 means OCP
  *   E4M3FN bytes (bias 7, no infinities, max finite 448).
- * - Nothing here is safe to run concurrently on two streams with the SAME
- *   workspace `ws`.
+ * - Two calls that share one workspace `ws` must not run concurrently (on
+ *   two streams); calls on one stream are ordered and may share it.
  */
 #ifndef DTA_H_
 #define DTA_H_
@@ -91,11 +91,12 @@ int attn_merge(const void* o_parts, const float* lse_parts, int n_parts,
  * previous step's. Per-thread float32 partial sums, a fixed-order float64
  * finish, so the result is bitwise reproducible. sum|b| = 0 gives the IEEE
  * quotient (+inf or NaN). The threshold compare stays with the caller.
+ * Enqueues two kernels (partials, then a one-workgroup finish).
  *
  * a, b  bf16 [n], 16-byte aligned; n >= 1
  * out   float, one device scalar, written
- * ws    device workspace of dta_ws_bytes() bytes, zero-filled by the caller
- *       before its first use; every call leaves it zero-filled again.
+ * ws    device workspace of at least dta_ws_bytes() bytes, 16-byte aligned;
+ *       scratch for the per-workgroup partials, no initialisation needed.
  */
 int residual_diff(const void* a, const void* b, int64_t n, float* out,
                   void* ws, hipStream_t stream);
@@ -111,6 +112,8 @@ int residual_diff(const void* a, const void* b, int64_t n, float* out,
  * x8       uint8 [n], 16-byte aligned, written
  * descale  float, one device scalar, written with s
  * ws       as for residual_diff (may be the same buffer, not concurrently)
+ * Enqueues three kernels: partial maxima, their one-workgroup finish into
+ * descale, and the cast.
  */
 int fp8_quant_per_tensor(const void* x, int64_t n, void* x8, float* descale,
                          void* ws, hipStream_t stream);
