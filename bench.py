@@ -104,7 +104,12 @@ def main():
     ap.add_argument("--video-reps", type=int, default=3)
     ap.add_argument("--no-video", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--legs", default="all",
+                    help="comma-separated subset of attn,chunks,merge,quant,fp8,residual "
+                         "(profiling runs only; the reported value needs all)")
     args = ap.parse_args()
+    legs_on = set(["attn", "chunks", "merge", "quant", "fp8", "residual"]
+                  if args.legs == "all" else args.legs.split(","))
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(the ring/Ulysses exchanges are out of scope); run with --gpus 1.",
@@ -147,30 +152,39 @@ def main():
     torch.cuda.synchronize()
 
     flop_full = attn_flop(B, H, N, N, D)
-    step_flop = 3 * flop_full
+    step_flop = flop_full * sum(1 for x in ("attn", "chunks", "fp8") if x in legs_on)
+    if "fp8" in legs_on and "quant" not in legs_on:
+        for x, x8_, i in ((q, q8, 0), (k, k8, 1), (v, v8, 2)):
+            dta.fp8_quant_per_tensor(x, x8_, ds[i:i + 1])
 
     def step(ev=None):
         if ev is not None:
             ev[0].record()
-        dta.attn_fwd(q, k, v, scale, o=o, lse=lse)
+        if "attn" in legs_on:
+            dta.attn_fwd(q, k, v, scale, o=o, lse=lse)
         if ev is not None:
             ev[1].record()
-        for i, (kc, vc) in enumerate(chunks):
-            dta.attn_fwd(q, kc, vc, scale, o=o_parts[i], lse=l_parts[i])
+        if "chunks" in legs_on:
+            for i, (kc, vc) in enumerate(chunks):
+                dta.attn_fwd(q, kc, vc, scale, o=o_parts[i], lse=l_parts[i])
         if ev is not None:
             ev[2].record()
-        dta.attn_merge(o_parts, l_parts, o=o_m, lse=l_m)
+        if "merge" in legs_on:
+            dta.attn_merge(o_parts, l_parts, o=o_m, lse=l_m)
         if ev is not None:
             ev[3].record()
-        dta.fp8_quant_per_tensor(q, q8, ds[0:1])
-        dta.fp8_quant_per_tensor(k, k8, ds[1:2])
-        dta.fp8_quant_per_tensor(v, v8, ds[2:3])
+        if "quant" in legs_on:
+            dta.fp8_quant_per_tensor(q, q8, ds[0:1])
+            dta.fp8_quant_per_tensor(k, k8, ds[1:2])
+            dta.fp8_quant_per_tensor(v, v8, ds[2:3])
         if ev is not None:
             ev[4].record()
-        dta.attn_fwd_fp8(q8, k8, v8, ds, scale, o=o8, lse=l8)
+        if "fp8" in legs_on:
+            dta.attn_fwd_fp8(q8, k8, v8, ds, scale, o=o8, lse=l8)
         if ev is not None:
             ev[5].record()
-        dta.residual_diff(ra, rb, out=rd)
+        if "residual" in legs_on:
+            dta.residual_diff(ra, rb, out=rd)
         if ev is not None:
             ev[6].record()
 
@@ -198,7 +212,7 @@ def main():
     torch.cuda.synchronize()
 
     def leg(a, b):
-        return sum(e[a].elapsed_time(e[b]) for e in evs) / len(evs)
+        return max(sum(e[a].elapsed_time(e[b]) for e in evs) / len(evs), 1e-6)
 
     ms_attn = leg(0, 1)
     ms_chunks = leg(1, 2)
@@ -229,6 +243,10 @@ def main():
                           "bytes": res_bytes, "cache": "warm"},
     }
 
+    leg_key = {"attn": "attn_fwd_bf16", "chunks": "attn_fwd_bf16_8_chunks",
+               "merge": "attn_merge", "quant": "fp8_quant_x3", "fp8": "attn_fwd_fp8",
+               "residual": "residual_diff"}
+    legs = {leg_key[x]: legs[leg_key[x]] for x in leg_key if x in legs_on}
     video = None
     if not args.no_video:
         del chunks

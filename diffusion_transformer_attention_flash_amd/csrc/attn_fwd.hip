@@ -21,20 +21,24 @@
 //   ds_read_b64_tr_b16, whose 16-lane 4x4 transposes hand each lane 4 keys of
 //   one head dimension; two such reads cover exactly the 8 keys the lane's P
 //   operand holds, so no shuffle of P is needed.
-// * K and V tiles (BN keys) are double-buffered in LDS with XOR-swizzled
-//   16-byte chunks (conflict-free for the 128-bit K reads and the transposing
-//   V reads); the next tile's global loads are issued before the current
-//   tile's MFMAs and stored to the other buffer after them: one barrier per
-//   tile.
+// * K and V tiles (BN keys) are double-buffered in LDS with padded rows: a
+//   16-byte pad puts the 16 K rows one 128-bit read quarter-wave touches in
+//   distinct bank groups, a 64-byte pad does the same for the 4 rows x 64
+//   bytes a half-wave of transposing V reads touches. Every operand address
+//   is then a per-lane base plus an immediate. The next tile's global loads
+//   are issued before the current tile's MFMAs and stored to the other buffer
+//   after them: one barrier per tile.
 // * Softmax runs in the log2 domain with c = scale*log2(e) folded into one FMA
 //   per score before v_exp_f32. The running max used for the exponent is only
 //   raised when some row's max grows by more than kTau (log2 units), so the
 //   O accumulator is rescaled rarely; p stays below 2^kTau, and O and l share
 //   the same reference max, so the result is exact.
-// * Only the last, partial K/V tile masks keys; its out-of-range rows are
-//   clamped loads of the last valid row, masked to zero weight.
+// * Only the last, partial K/V tile masks keys; its rows past Nkv fail the
+//   buffer range check, read as zero and get zero weight.
 // * Workgroup ids are remapped so that the workgroups of one XCD walk
 //   consecutive query tiles of the same head and share K/V through its L2.
+
+#include <type_traits>
 
 #include "common.h"
 
@@ -49,7 +53,8 @@ struct AttnCfg {
   static constexpr int kBM = NW * 32;               // query rows per workgroup
   static constexpr int kCPR = D / 8;                // 16-byte chunks per row
   static constexpr int kRP = 16 / kCPR;             // rows per 256 bytes
-  static constexpr int kTileElems = BN * D;
+  static constexpr int kKS = D + 8;                 // K row stride (elements)
+  static constexpr int kVS = D + 32;                // V row stride (elements)
   static constexpr int kChunks = BN * kCPR;         // chunks per tile
   static constexpr int kCpt = kChunks / kThreads;   // chunks per thread
   static_assert(kChunks % kThreads == 0, "tile must split evenly");
@@ -57,21 +62,8 @@ struct AttnCfg {
 };
 
 constexpr float kTau = 8.0f;
-
-// Physical 16-byte chunk of logical chunk `c` in row `r` of the K tile: the
-// 16 rows one 128-bit read wave-quarter touches land in distinct bank groups.
-template <int D>
-__device__ __forceinline__ int k_swz(int r, int c) {
-  constexpr int kCPR = D / 8, kRP = 16 / kCPR;
-  return c ^ ((r / kRP) % kCPR);
-}
-// Same for the V tile, read by ds_read_b64_tr_b16: 4 consecutive rows x 4
-// consecutive chunks per half-wave must hit distinct bank groups.
-template <int D>
-__device__ __forceinline__ int v_swz(int r, int c) {
-  constexpr int kCPR = D / 8, kRP = 16 / kCPR;
-  return c ^ (4 * ((r / kRP) % (kCPR / 4)));
-}
+// Fourth dword of a raw buffer resource (32-bit data format, no swizzle).
+constexpr int kBufDword3 = 0x00020000;
 
 __device__ __forceinline__ float xhalf_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
@@ -90,8 +82,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
     float* __restrict__ lse, int Nq, int Nkv, float c, int n_qt) {
   using C = AttnCfg<D, NW, BN>;
-  __shared__ __attribute__((aligned(16))) uint16_t ks[2][C::kTileElems];
-  __shared__ __attribute__((aligned(16))) uint16_t vs[2][C::kTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t ks[2][BN * C::kKS];
+  __shared__ __attribute__((aligned(16))) uint16_t vs[2][BN * C::kVS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -112,40 +104,40 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(
                         : bf16x8{};
 
   // Tile staging: chunk ci -> row ci / kCPR, logical chunk ci % kCPR; 16
-  // consecutive threads cover 256 contiguous bytes of global memory.
+  // consecutive threads cover 256 contiguous bytes of global memory. Loads go
+  // through buffer resources whose base and byte range are the tile's: the
+  // per-lane offsets stay constant, the address arithmetic is scalar, and rows
+  // past Nkv fail the range check and read as zero.
   u32x4 kreg[C::kCpt], vreg[C::kCpt];
+  const int st_r = tid / C::kCPR, st_c = tid % C::kCPR;   // row/chunk of it = 0
+  constexpr int kRowsPerIt = C::kThreads / C::kCPR;
   auto load_tile = [&](int j) {
-    const int key0 = j * BN;
+    const int64_t key0 = (int64_t)j * BN;
+    const int bytes = (int)min<int64_t>((int64_t)(Nkv - key0) * D * 2, (int64_t)BN * D * 2);
+    const __amdgpu_buffer_rsrc_t kr =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(kh + key0 * D), 0, bytes, kBufDword3);
+    const __amdgpu_buffer_rsrc_t vr =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(vh + key0 * D), 0, bytes, kBufDword3);
 #pragma unroll
     for (int it = 0; it < C::kCpt; ++it) {
-      const int ci = it * C::kThreads + tid;
-      const int r = ci / C::kCPR, cc = ci % C::kCPR;
-      const int64_t gr = min(key0 + r, Nkv - 1);
-      kreg[it] = *reinterpret_cast<const u32x4*>(kh + gr * D + cc * 8);
-      vreg[it] = *reinterpret_cast<const u32x4*>(vh + gr * D + cc * 8);
+      const int off = ((st_r + it * kRowsPerIt) * D + st_c * 8) * 2;
+      kreg[it] = __builtin_amdgcn_raw_buffer_load_b128(kr, off, 0, 0);
+      vreg[it] = __builtin_amdgcn_raw_buffer_load_b128(vr, off, 0, 0);
     }
   };
   auto store_tile = [&](int buf) {
 #pragma unroll
     for (int it = 0; it < C::kCpt; ++it) {
-      const int ci = it * C::kThreads + tid;
-      const int r = ci / C::kCPR, cc = ci % C::kCPR;
-      *reinterpret_cast<u32x4*>(&ks[buf][r * D + k_swz<D>(r, cc) * 8]) = kreg[it];
-      *reinterpret_cast<u32x4*>(&vs[buf][r * D + v_swz<D>(r, cc) * 8]) = vreg[it];
+      const int r = st_r + it * kRowsPerIt;
+      *reinterpret_cast<u32x4*>(&ks[buf][r * C::kKS + st_c * 8]) = kreg[it];
+      *reinterpret_cast<u32x4*>(&vs[buf][r * C::kVS + st_c * 8]) = vreg[it];
     }
   };
 
-  // Per-lane constants of the operand reads.
-  int k_off[BN / 32][D / 16];            // element offset of the K A-operand chunk
-#pragma unroll
-  for (int kb = 0; kb < BN / 32; ++kb)
-#pragma unroll
-    for (int ds = 0; ds < D / 16; ++ds) {
-      const int r = kb * 32 + l32;
-      k_off[kb][ds] = r * D + k_swz<D>(r, 2 * ds + g) * 8;
-    }
-  const int vr_lo = 4 * g + ((lane & 15) >> 2);   // key offset inside 8-key group
-  const int vd_lo = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);  // dim offset in 32
+  // Per-lane bases of the operand reads; everything else is an immediate.
+  const int k_base = l32 * C::kKS + g * 8;
+  const int v_base = (4 * g + ((lane & 15) >> 2)) * C::kVS +
+                     16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
   f32x16 oacc[D / 32];
 #pragma unroll
@@ -157,8 +149,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(
   store_tile(0);
   __syncthreads();
 
-  for (int j = 0; j < n_tiles; ++j) {
-    const int buf = j & 1;
+  // One K/V tile: MASK is set only for the last tile when Nkv % BN != 0.
+  auto tile = [&](int j, auto buf_tag, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    constexpr int buf = decltype(buf_tag)::value;
     const bool has_next = j + 1 < n_tiles;
     if (has_next) load_tile(j + 1);
     const uint16_t* kt = ks[buf];
@@ -172,14 +166,14 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(
     for (int ds = 0; ds < D / 16; ++ds)
 #pragma unroll
       for (int kb = 0; kb < BN / 32; ++kb) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt + k_off[kb][ds]);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+            kt + k_base + kb * 32 * C::kKS + ds * 16);
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qr[ds], s[kb], 0, 0, 0);
       }
 
     // Online softmax in the log2 domain.
-    const bool tail = (j + 1) * BN > Nkv;
     const int key_lim = Nkv - j * BN;
-    if (tail) {
+    if constexpr (MASK) {
 #pragma unroll
       for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
@@ -211,11 +205,16 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(
         for (int i = 0; i < 8; ++i) {
           const int r = 8 * t + i;
           p[i] = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c, -m_run));
-          if (tail && kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3) >= key_lim) p[i] = 0.f;
+          if constexpr (MASK) {
+            if (kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3) >= key_lim) p[i] = 0.f;
+          }
           rs += p[i];
         }
         pb[kb][t] = bf16x8{(__bf16)p[0], (__bf16)p[1], (__bf16)p[2], (__bf16)p[3],
                            (__bf16)p[4], (__bf16)p[5], (__bf16)p[6], (__bf16)p[7]};
+        // Keep the row sum next to the exponentials: the float32 p values
+        // then die here instead of living across the P.V MFMAs.
+        asm volatile("" : "+v"(rs));
       }
     l_run += rs;
 
@@ -229,11 +228,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(
           s16x4 part[2];
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
-            const int r = kb * 32 + 16 * t + 8 * h + vr_lo;
-            const int d = db * 32 + vd_lo;
-            const int off = r * D + v_swz<D>(r, d >> 3) * 8 + (d & 7);
-            part[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_s16x4*)(vt + off));
+            const int off = v_base + (kb * 32 + 16 * t + 8 * h) * C::kVS + db * 32;
+            part[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vt + off));
           }
           const s16x4 lo = part[0], hi = part[1];
           const bf16x8 a = __builtin_bit_cast(
@@ -244,6 +240,22 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(
 
     if (has_next) store_tile(buf ^ 1);
     __syncthreads();
+  };
+
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  const int n_full = (Nkv % BN == 0) ? n_tiles : n_tiles - 1;
+  int j = 0;
+  for (; j + 1 < n_full; j += 2) {
+    tile(j, B0{}, std::false_type{});
+    tile(j + 1, B1{}, std::false_type{});
+  }
+  if (j < n_full) tile(j++, B0{}, std::false_type{});
+  if (j < n_tiles) {
+    if (j & 1)
+      tile(j, B1{}, std::true_type{});
+    else
+      tile(j, B0{}, std::true_type{});
   }
 
   // Epilogue: lane owns query `row` and dims db*32 + 8*(r/4) + 4g + r%4.
