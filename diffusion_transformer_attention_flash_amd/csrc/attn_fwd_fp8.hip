@@ -3,22 +3,41 @@
 // into the attention itself), for gfx950.
 //
 //   s_ij = scale * s_q * s_k * (q8_i . k8_j)             fp8 MFMA, fp32 acc
-//   p_ij = exp(s_ij - m_i)       m_i = running row max of the online softmax
-//   P8   = e4m3(448 * p_ij)                              P quantised to fp8
-//   O_i  = s_v * sum_j P8_ij v8_j / (448 * l_i),  l_i = sum_j p_ij (fp32)
+//   p_ij = exp(s_ij - m_i)   m_i = the online softmax's reference max, which
+//                            trails the running row max by at most 2 bits:
+//                            p_ij <= 4
+//   P8   = e4m3(108 * p_ij)                 P quantised to fp8, <= 432
+//   O_i  = s_v * sum_j P8_ij v8_j / (108 * l_i),  l_i = sum_j p_ij (fp32)
 //   LSE_i = m_i + ln l_i
 //
-// Same structure as the bf16 kernel (S^T = K . Q^T with one query per lane,
-// O^T += V^T . P^T, double-buffered K/V tiles in LDS, XCD-aware tile order),
-// on v_mfma_scale_f32_32x32x64_f8f6f4 with both operands in E4M3 and unit
-// block scales: one instruction contracts 64 values. The 32 E4M3 values a
-// lane supplies for P^T are its 32 exponentiated scores of the 64-key tile,
-// so V^T is stored in LDS with the key bits permuted to match: the 32 keys
-// of a lane half are then 32 consecutive bytes of one V^T row.
+// Same structure as the bf16 kernel: S^T = K . Q^T with one query per lane,
+// O^T += V^T . P^T, double-buffered padded K/V tiles in LDS fed by buffer
+// loads whose range check zero-fills rows past Nkv, a peeled masked tail
+// tile, a reference max raised only when a row outgrows it, XCD-aware tile
+// order.
+// The MFMA is v_mfma_f32_32x32x64_f8f6f4 with both operands E4M3: one
+// instruction contracts 64 values, so a 64-key tile takes one P.V MFMA per 32
+// head dims.
+// * 108 p is produced directly as exp2(c s - (m - log2 108)), so quantising
+//   P costs only the packed conversion; the row sum of these values is
+//   108 l. The 2-bit slack of the reference max keeps the O rescale rare
+//   while 108 p stays inside the E4M3 range with a 3.7% margin for the
+//   rounding of v_exp_f32 (the largest finite E4M3 value is 448).
+// * The P^T operand of lane half g is its 32 scores of the tile in register
+//   order, i.e. keys 32(i/16) + 8((i%16)/4) + 4g + i%4 for byte i. The V tile
+//   is written to LDS with its key index permuted (key bit 2 -> row bit 5,
+//   key bits 3-5 -> row bits 2-4), so those 32 keys are rows 32g .. 32g+31,
+//   and four ds_read_b64_tr_b8 -- each handing a lane one head dimension of
+//   8 consecutive rows -- assemble the V^T operand in the same byte order.
+
+#include <type_traits>
 
 #include "common.h"
 
 namespace dta {
+
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 
 template <int D, int NW>
 struct Fp8Cfg {
@@ -26,25 +45,40 @@ struct Fp8Cfg {
   static constexpr int kThreads = NW * 64;
   static constexpr int kBM = NW * 32;
   static constexpr int kKS = D + 16;                 // K row stride (bytes)
-  static constexpr int kVS = kBN + 16;               // V^T row stride (bytes)
-  static constexpr int kChunks = kBN * D / 16;       // 16-byte chunks per tile
+  static constexpr int kVS = D + 32;                 // V row stride (bytes)
+  static constexpr int kCPR = D / 16;                // 16-byte chunks per row
+  static constexpr int kChunks = kBN * kCPR;
   static constexpr int kCpt = kChunks / kThreads;
   static_assert(kChunks % kThreads == 0, "tile must split evenly");
 };
 
-// Byte position of key `key` (0..63) in a V^T row. A key 32kb + 8j + 4g + i
-// (kb = bit 5, j = bits 3-4, g = bit 2, i = bits 0-1) goes to 32g + 16kb +
-// 4j + i, the slot the P^T operand of lane half g holds it in.
-__device__ __forceinline__ int vt8_pos(int key) {
-  const int kb = (key >> 5) & 1, j = (key >> 3) & 3, g = (key >> 2) & 1, i = key & 3;
-  return 32 * g + 16 * kb + 4 * j + i;
+constexpr float kTau8 = 2.0f;                    // reference-max slack (log2)
+constexpr float kLog2PScale = 6.754887502163468f; // log2(108): 108 * 2^kTau8 <= 448
+constexpr int kBufDword3Fp8 = 0x00020000;
+
+// LDS row of key `key` (0..63) in the V tile.
+__device__ __forceinline__ int v8_row(int key) {
+  return (((key >> 2) & 1) << 5) | (((key >> 3) & 7) << 2) | (key & 3);
 }
 
-// Unit E8M0 block scale (2^0) for both MFMA operands.
-constexpr int kUnitScale = 127;
+__device__ __forceinline__ float xhalf_max8(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_sum8(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ i32x8 cat8(u32x4 lo, u32x4 hi) {
+  return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+               (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+}
 
 template <int D, int NW>
-__global__ __launch_bounds__(NW * 64) void attn_fwd_fp8_kernel(
+__global__ __launch_bounds__(NW * 64, 2) void attn_fwd_fp8_kernel(
     const uint8_t* __restrict__ q, const uint8_t* __restrict__ k,
     const uint8_t* __restrict__ v, const float* __restrict__ descale,
     uint16_t* __restrict__ o, float* __restrict__ lse, int Nq, int Nkv,
@@ -52,7 +86,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_fp8_kernel(
   using C = Fp8Cfg<D, NW>;
   constexpr int BN = C::kBN;
   __shared__ __attribute__((aligned(16))) uint8_t ks[2][BN * C::kKS];
-  __shared__ __attribute__((aligned(16))) uint8_t vts[2][D * C::kVS];
+  __shared__ __attribute__((aligned(16))) uint8_t vs[2][BN * C::kVS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -60,58 +94,58 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_fp8_kernel(
   const int blk = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = blk / n_qt, qt = blk - bh * n_qt;
   const int64_t q_base = (int64_t)bh * Nq * D;
-  const int64_t kv_base = (int64_t)bh * Nkv * D;
+  const uint8_t* kh = k + (int64_t)bh * Nkv * D;
+  const uint8_t* vh = v + (int64_t)bh * Nkv * D;
   const int row = qt * C::kBM + wave * 32 + l32;
 
   const float s_q = descale[0], s_k = descale[1], s_v = descale[2];
   const float c = scale * s_q * s_k * kLog2e;
 
-  // Q^T operand: 32 bytes (dims ks*64 + 32g .. +31) per 64-dim step.
+  // Q^T operand: 32 bytes (dims kk*64 + 32g .. +31) per 64-dim step.
   i32x8 qr[D / 64];
 #pragma unroll
   for (int kk = 0; kk < D / 64; ++kk) {
     if (row < Nq) {
       const u32x4* src = reinterpret_cast<const u32x4*>(
           q + q_base + (int64_t)row * D + kk * 64 + g * 32);
-      const u32x4 lo = src[0], hi = src[1];
-      qr[kk] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                     (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      qr[kk] = cat8(src[0], src[1]);
     } else {
       qr[kk] = i32x8{};
     }
   }
 
+  // Staging: chunk ci -> key ci / kCPR, 16-byte chunk ci % kCPR.
+  const int st_r = tid / C::kCPR, st_c = tid % C::kCPR;
+  constexpr int kRowsPerIt = C::kThreads / C::kCPR;
   u32x4 kreg[C::kCpt], vreg[C::kCpt];
   auto load_tile = [&](int j) {
-    const int key0 = j * BN;
+    const int64_t key0 = (int64_t)j * BN;
+    const int bytes = (int)min<int64_t>((int64_t)(Nkv - key0) * D, (int64_t)BN * D);
+    const __amdgpu_buffer_rsrc_t kr =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(kh + key0 * D), 0, bytes, kBufDword3Fp8);
+    const __amdgpu_buffer_rsrc_t vr =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(vh + key0 * D), 0, bytes, kBufDword3Fp8);
 #pragma unroll
     for (int it = 0; it < C::kCpt; ++it) {
-      const int ci = it * C::kThreads + tid;
-      const int kk = ci / (D / 16), kd = ci % (D / 16);
-      const int vk = ci % BN, vd = ci / BN;
-      kreg[it] = (key0 + kk < Nkv)
-                     ? *reinterpret_cast<const u32x4*>(
-                           k + kv_base + (int64_t)(key0 + kk) * D + kd * 16)
-                     : u32x4{0, 0, 0, 0};
-      vreg[it] = (key0 + vk < Nkv)
-                     ? *reinterpret_cast<const u32x4*>(
-                           v + kv_base + (int64_t)(key0 + vk) * D + vd * 16)
-                     : u32x4{0, 0, 0, 0};
+      const int off = (st_r + it * kRowsPerIt) * D + st_c * 16;
+      kreg[it] = __builtin_amdgcn_raw_buffer_load_b128(kr, off, 0, 0);
+      vreg[it] = __builtin_amdgcn_raw_buffer_load_b128(vr, off, 0, 0);
     }
   };
   auto store_tile = [&](int buf) {
 #pragma unroll
     for (int it = 0; it < C::kCpt; ++it) {
-      const int ci = it * C::kThreads + tid;
-      const int kk = ci / (D / 16), kd = ci % (D / 16);
-      const int vk = ci % BN, vd = ci / BN;
-      *reinterpret_cast<u32x4*>(&ks[buf][kk * C::kKS + kd * 16]) = kreg[it];
-      uint8_t* dst = &vts[buf][(vd * 16) * C::kVS + vt8_pos(vk)];
-#pragma unroll
-      for (int e = 0; e < 16; ++e)
-        dst[e * C::kVS] = (uint8_t)((vreg[it][e >> 2] >> (8 * (e & 3))) & 0xFF);
+      const int r = st_r + it * kRowsPerIt;
+      *reinterpret_cast<u32x4*>(&ks[buf][r * C::kKS + st_c * 16]) = kreg[it];
+      *reinterpret_cast<u32x4*>(&vs[buf][v8_row(r) * C::kVS + st_c * 16]) = vreg[it];
     }
   };
+
+  // Operand read bases: K rows l32 (A operand), V^T rows 32g + 8a + s/2 at
+  // byte 16*(lane/16 % 2) + 8*(s%2) of a 32-dim block, s = lane % 16.
+  const int k_base = l32 * C::kKS + g * 32;
+  const int v_base = (32 * g + ((lane & 15) >> 1)) * C::kVS + 16 * ((lane >> 4) & 1) +
+                     8 * (lane & 1);
 
   f32x16 oacc[D / 32];
 #pragma unroll
@@ -123,48 +157,47 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_fp8_kernel(
   store_tile(0);
   __syncthreads();
 
-  for (int j = 0; j < n_tiles; ++j) {
-    const int buf = j & 1;
+  auto tile = [&](int j, auto buf_tag, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    constexpr int buf = decltype(buf_tag)::value;
     const bool has_next = j + 1 < n_tiles;
     if (has_next) load_tile(j + 1);
     const uint8_t* kt = ks[buf];
-    const uint8_t* vt = vts[buf];
+    const uint8_t* vt = vs[buf];
 
     f32x16 s[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-    for (int kk = 0; kk < D / 64; ++kk) {
+    for (int kk = 0; kk < D / 64; ++kk)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const u32x4* src = reinterpret_cast<const u32x4*>(
-            &kt[(kb * 32 + l32) * C::kKS + kk * 64 + g * 32]);
-        const u32x4 lo = src[0], hi = src[1];
-        const i32x8 a = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                         (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        const u32x4* src = reinterpret_cast<const u32x4*>(kt + k_base + kb * 32 * C::kKS + kk * 64);
         s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            a, qr[kk], s[kb], 0, 0, 0, kUnitScale, 0, kUnitScale);
+            cat8(src[0], src[1]), qr[kk], s[kb], 0, 0, 0, 0, 0, 0);
       }
-    }
 
-    const bool tail = (j + 1) * BN > Nkv;
     const int key_lim = Nkv - j * BN;
-    float mx = -INFINITY;
-    if (tail) {
+    if constexpr (MASK) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-          if (key >= key_lim) s[kb][r] = -INFINITY;
-        }
+        for (int r = 0; r < 16; ++r)
+          if (kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3) >= key_lim) s[kb][r] = -INFINITY;
     }
+    float mx = s[0][0];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx * c);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
+    mx = xhalf_max8(mx) * c;
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + kTau8) != 0) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
+    }
+    const float m448 = m_run - kLog2PScale;
     float rs = 0.f;
     i32x8 pb;
 #pragma unroll
@@ -175,39 +208,55 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_fp8_kernel(
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int r = 4 * w + u;
-          float x = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c, -m_new));
-          if (tail) {
-            const int key = kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-            if (key >= key_lim) x = 0.f;
+          p[u] = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c, -m448));
+          if constexpr (MASK) {
+            if (kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3) >= key_lim) p[u] = 0.f;
           }
-          rs += x;
-          p[u] = x * 448.0f;
+          rs += p[u];
         }
         int wd = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
         wd = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], wd, true);
         pb[kb * 4 + w] = wd;
+        asm volatile("" : "+v"(rs));
       }
-    l_run = l_run * alpha + rs;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
+    l_run += rs;
 
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
-      const u32x4* src = reinterpret_cast<const u32x4*>(
-          &vt[(db * 32 + l32) * C::kVS + g * 32]);
-      const u32x4 lo = src[0], hi = src[1];
-      const i32x8 a = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                       (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-      oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-          a, pb, oacc[db], 0, 0, 0, kUnitScale, 0, kUnitScale);
+      i32x2 part[4];
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+        part[a] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (lds_i32x2*)(vt + v_base + 8 * a * C::kVS + db * 32));
+      const i32x8 av = {part[0][0], part[0][1], part[1][0], part[1][1],
+                        part[2][0], part[2][1], part[3][0], part[3][1]};
+      oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, pb, oacc[db], 0, 0, 0, 0,
+                                                                  0, 0);
     }
 
     if (has_next) store_tile(buf ^ 1);
     __syncthreads();
+  };
+
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  const int n_full = (Nkv % BN == 0) ? n_tiles : n_tiles - 1;
+  int j = 0;
+  for (; j + 1 < n_full; j += 2) {
+    tile(j, B0{}, std::false_type{});
+    tile(j + 1, B1{}, std::false_type{});
+  }
+  if (j < n_full) tile(j++, B0{}, std::false_type{});
+  if (j < n_tiles) {
+    if (j & 1)
+      tile(j, B1{}, std::true_type{});
+    else
+      tile(j, B0{}, std::true_type{});
   }
 
-  const float lt = l_run + __shfl_xor(l_run, 32, 64);
-  const float f = s_v / (448.0f * lt);
+  // l_run holds 108 l; O = s_v * acc / (108 l).
+  const float lt = xhalf_sum8(l_run);
+  const float f = s_v / lt;
   if (row < Nq) {
     uint16_t* orow = o + q_base + (int64_t)row * D;
 #pragma unroll
@@ -220,7 +269,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_fp8_kernel(
         *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * jj + 4 * g) = w;
       }
     if (g == 0 && lse != nullptr)
-      lse[(int64_t)bh * Nq + row] = (m_run + log2f(lt)) * kLn2;
+      lse[(int64_t)bh * Nq + row] = (m_run + log2f(lt) - kLog2PScale) * kLn2;
   }
 }
 

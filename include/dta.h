@@ -122,9 +122,11 @@ int fp8_quant_per_tensor(const void* x, int64_t n, void* x8, float* descale,
  * attn_fwd_fp8 -- the fp8 dynamic-quantisation variant of attn_fwd: Q, K, V
  * are E4M3FN with per-tensor scales (as fp8_quant_per_tensor writes them);
  * S = scale * s_q s_k (Q8 . K8^T) on fp8 MFMA with float32 accumulation;
- * p = exp(s - m) is quantised to E4M3FN at x448 before the P.V product;
- * O = (P8 . V8) s_v / (448 l) with l the float32 sum of the unquantised p;
- * LSE = m + ln l. m is the running row maximum of the online softmax.
+ * p = exp(s - m) is quantised to E4M3FN at x108 before the P.V product,
+ * where m is the online softmax's reference max, kept within a factor 4 of
+ * the running row max so that 108 p <= 432 (E4M3's largest value is 448);
+ * O = (P8 . V8) s_v / (108 l) with l the float32 sum of the unquantised p;
+ * LSE = m + ln l.
  *
  * q8, k8, v8  E4M3FN bytes, layouts as attn_fwd, 16-byte aligned
  * descale     device float[3] = {s_q, s_k, s_v}
