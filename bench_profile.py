@@ -6,10 +6,11 @@
         WRITE_SIZE counters to bytes.
     python bench_profile.py summarize-trace DIR OUT.md --cmd "..."
         Turns a `rocprofv3 --kernel-trace --stats -f csv` directory into a
-        short markdown table (calls, average and total time per kernel).
+        short markdown table (launches, average, median and total time per
+        kernel, grid and position in a run of back-to-back launches).
     python bench_profile.py summarize-pmc --fetch DIR --write DIR
-            --copy-fetch DIR --copy-write DIR --kernel REGEX --grid N
-            --out OUT.json --cmd "..."
+            --copy-fetch DIR --copy-write DIR --kernel REGEX [--grid N]
+            [--first-of-run] --out OUT.json --cmd "..."
         Per-launch HBM bytes of one kernel from FETCH_SIZE / WRITE_SIZE runs,
         each scaled by what the same counter reads for the copy above.
 """
@@ -53,48 +54,72 @@ def _col(row, *keys):
 
 
 def cmd_summarize_trace(args):
+    """Per-kernel statistics from the kernel trace. Launches of one kernel
+    that follow each other directly form a run; the first launch of a run is
+    reported apart from the rest (bench.py's step launches the full-K/V
+    attention first, then the 8 chunk attentions with the same grid)."""
     rows = []
-    for path in _find(args.dir, "kernel_stats.csv"):
+    for path in _find(args.dir, "kernel_trace.csv"):
         with open(path) as f:
             rows += list(csv.DictReader(f))
     if not rows:
-        raise SystemExit("empty stats")
-    kn = _col(rows[0], "name")
-    kc = _col(rows[0], "calls")
-    kt = _col(rows[0], "totaldurationns")
-    ka = _col(rows[0], "averagens")
-    lines = ["# rocprofv3 kernel statistics: %s" % args.title, "",
+        raise SystemExit("empty trace")
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    groups = {}
+    prev = None
+    pos = 0
+    for r in rows:
+        name = r["Kernel_Name"]
+        pos = pos + 1 if name == prev else 0
+        prev = name
+        grid = r.get("Grid_Size_X") or r.get("Grid_Size") or "?"
+        key = (name, grid, "first of run" if pos == 0 else "later in run")
+        groups.setdefault(key, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    lines = ["# rocprofv3 kernel trace: %s" % args.title, "",
              "Command (repo root): `%s`" % args.cmd, "",
-             "| kernel | calls | average (us) | total (ms) |", "|---|---:|---:|---:|"]
-    for r in sorted(rows, key=lambda r: -float(r[kt])):
-        name = r[kn]
-        if len(name) > 110:
-            name = name[:107] + "..."
-        lines.append("| `%s` | %s | %.2f | %.3f |" % (name, r[kc], float(r[ka]) / 1e3,
-                                                     float(r[kt]) / 1e6))
+             "| kernel | grid (threads) | launches | calls | average (us) | median (us) | total (ms) |",
+             "|---|---:|---|---:|---:|---:|---:|"]
+    for (name, grid, where), d in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        short = name if len(name) <= 90 else name[:87] + "..."
+        d_sorted = sorted(d)
+        lines.append("| `%s` | %s | %s | %d | %.2f | %.2f | %.3f |" % (
+            short, grid, where, len(d), statistics.mean(d) / 1e3,
+            d_sorted[len(d) // 2] / 1e3, sum(d) / 1e6))
     with open(args.out, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
 
-def _pmc_values(d, counter, kernel_re, grid=None):
-    """Counter value per dispatch of kernels matching kernel_re (and grid)."""
-    vals = []
+def _pmc_values(d, counter, kernel_re, grid=None, first_of_run=False):
+    """Counter value per dispatch of kernels matching kernel_re (and grid).
+    With first_of_run, only dispatches that start a run of consecutive
+    dispatches of the same kernel count (see cmd_summarize_trace)."""
+    rows = []
     for path in _find(d, "counter_collection.csv"):
         with open(path) as f:
             for r in csv.DictReader(f):
-                if r.get(_col(r, "counter", "name")) != counter:
-                    continue
-                if not re.search(kernel_re, r[_col(r, "kernel", "name")]):
-                    continue
-                if grid is not None:
-                    try:
-                        g = int(r[_col(r, "grid", "size")])
-                    except KeyError:
-                        g = None
-                    if g is not None and g != grid:
-                        continue
-                vals.append(float(r[_col(r, "counter", "value")]))
+                if r.get(_col(r, "counter", "name")) == counter:
+                    rows.append(r)
+    if not rows:
+        raise SystemExit("no %s rows in %s" % (counter, d))
+    did = _col(rows[0], "dispatch", "id")
+    rows.sort(key=lambda r: int(r[did]))
+    vals, prev = [], None
+    kn = _col(rows[0], "kernel", "name")
+    for r in rows:
+        name = r[kn]
+        first = name != prev
+        prev = name
+        if not re.search(kernel_re, name) or (first_of_run and not first):
+            continue
+        if grid is not None:
+            try:
+                g = int(r[_col(r, "grid", "size")])
+            except KeyError:
+                g = None
+            if g is not None and g != grid:
+                continue
+        vals.append(float(r[_col(r, "counter", "value")]))
     if not vals:
         raise SystemExit("no %s rows for /%s/ in %s" % (counter, kernel_re, d))
     return vals
@@ -106,13 +131,16 @@ def cmd_summarize_pmc(args):
     cw = statistics.median(_pmc_values(args.copy_write, "WRITE_SIZE", args.copy_kernel))
     f_fetch = copy_kib / cf
     f_write = copy_kib / cw
-    kf = statistics.median(_pmc_values(args.fetch, "FETCH_SIZE", args.kernel, args.grid))
-    kw = statistics.median(_pmc_values(args.write, "WRITE_SIZE", args.kernel, args.grid))
+    kf = statistics.median(_pmc_values(args.fetch, "FETCH_SIZE", args.kernel, args.grid,
+                                       args.first_of_run))
+    kw = statistics.median(_pmc_values(args.write, "WRITE_SIZE", args.kernel, args.grid,
+                                       args.first_of_run))
     sys.path.insert(0, ROOT)
     from bench import kernel_source_hash
     out = {
         "kernel": args.kernel,
         "grid_size": args.grid,
+        "first_of_run_only": args.first_of_run,
         "kernel_source_hash": kernel_source_hash(),
         "fetch_kib_per_launch_raw": kf,
         "write_kib_per_launch_raw": kw,
@@ -146,7 +174,8 @@ def main():
     p = sub.add_parser("summarize-pmc")
     for a in ("--fetch", "--write", "--copy-fetch", "--copy-write", "--kernel", "--out", "--cmd"):
         p.add_argument(a, required=True)
-    p.add_argument("--copy-kernel", default="copy|elementwise")
+    p.add_argument("--copy-kernel", default="copyBuffer")
+    p.add_argument("--first-of-run", action="store_true")
     p.add_argument("--copy-mib", type=int, default=1024)
     p.add_argument("--grid", type=int, default=None)
     args = ap.parse_args()

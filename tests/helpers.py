@@ -21,6 +21,10 @@ RESIDUAL_REL = 1e-4
 O_REL_L2 = 1e-2
 FP8_REL_L2_VS_BF16 = 0.10
 FP8_REL_L2_VS_DEQUANT = 0.05
+# Peaked rows (logit spread x4) amplify the E4M3 rounding of Q and K into the
+# logits, so the total fp8 error against the bf16-input oracle doubles; the
+# kernel-arithmetic gate against the dequantised oracle stays at 0.05.
+FP8_REL_L2_VS_BF16_PEAKED = 0.20
 
 
 def to64(t):

@@ -7,8 +7,8 @@ import torch
 import diffusion_transformer_attention_flash_amd as dta
 import oracle
 import workloads
-from helpers import (FP8_O_MEAN_ABS, FP8_REL_L2_VS_BF16, FP8_REL_L2_VS_DEQUANT,
-                     LSE_ABS, rel_l2, to64)
+from helpers import (FP8_O_MEAN_ABS, FP8_REL_L2_VS_BF16, FP8_REL_L2_VS_BF16_PEAKED,
+                     FP8_REL_L2_VS_DEQUANT, LSE_ABS, rel_l2, to64)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -22,7 +22,8 @@ def _quant3(q, k, v):
     return q8, k8, v8, ds
 
 
-def _check(o8, l8, q, k, v, q8, k8, v8, ds, scale, rows=None, what=""):
+def _check(o8, l8, q, k, v, q8, k8, v8, ds, scale, rows=None, what="",
+           gate_bf16=FP8_REL_L2_VS_BF16):
     dsc = ds.cpu().tolist()
     o_dq, l_dq = oracle.attention_fp8(q8.cpu().numpy(), k8.cpu().numpy(), v8.cpu().numpy(),
                                       dsc, scale, rows=rows)
@@ -40,7 +41,7 @@ def _check(o8, l8, q, k, v, q8, k8, v8, ds, scale, rows=None, what=""):
         what, mean_abs, r_bf, r_dq, e_l)
     print(msg)
     assert mean_abs <= FP8_O_MEAN_ABS, msg
-    assert r_bf <= FP8_REL_L2_VS_BF16, msg
+    assert r_bf <= gate_bf16, msg
     assert r_dq <= FP8_REL_L2_VS_DEQUANT, msg
     assert e_l <= LSE_ABS, msg
 
@@ -62,7 +63,8 @@ def test_fp8_attention_peaked():
     q8, k8, v8, ds = _quant3(q, k, v)
     o8, l8 = dta.attn_fwd_fp8(q8, k8, v8, ds, 128 ** -0.5)
     torch.cuda.synchronize()
-    _check(o8, l8, q, k, v, q8, k8, v8, ds, 128 ** -0.5, what="fp8 peaked")
+    _check(o8, l8, q, k, v, q8, k8, v8, ds, 128 ** -0.5, what="fp8 peaked",
+           gate_bf16=FP8_REL_L2_VS_BF16_PEAKED)
 
 
 def test_fp8_flux_1024_sampled_rows():
