@@ -247,6 +247,34 @@ def main():
                "merge": "attn_merge", "quant": "fp8_quant_x3", "fp8": "attn_fwd_fp8",
                "residual": "residual_diff"}
     legs = {leg_key[x]: legs[leg_key[x]] for x in leg_key if x in legs_on}
+
+    # The same ring with the merge fused into each step (attn_fwd_accum): the
+    # first chunk by attn_fwd, the other seven folded into one running (o, lse).
+    # Timed apart from the step, which keeps the separate partials + merge.
+    if "chunks" in legs_on:
+        o_r = torch.empty_like(q)
+        l_r = torch.empty_like(lse)
+
+        def ring():
+            dta.attn_fwd(q, chunks[0][0], chunks[0][1], scale, o=o_r, lse=l_r)
+            for kc, vc in chunks[1:]:
+                dta.attn_fwd_accum(q, kc, vc, o_r, l_r, scale)
+
+        for _ in range(3):
+            ring()
+        torch.cuda.synchronize()
+        ra_ev, rb_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ra_ev.record()
+        for _ in range(args.steps):
+            ring()
+        rb_ev.record()
+        torch.cuda.synchronize()
+        ms_ring = ra_ev.elapsed_time(rb_ev) / args.steps
+        legs["ring_fused_8_steps"] = {
+            "ms": ms_ring, "TFLOP/s": flop_full / (ms_ring * 1e-3) / 1e12,
+            "vs_chunks_plus_merge_ms": ms_chunks + ms_merge,
+            "in_step": False}
+        del o_r, l_r
     video = None
     if not args.no_video:
         del chunks

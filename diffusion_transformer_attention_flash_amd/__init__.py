@@ -18,7 +18,8 @@ import torch
 from . import _lib
 from ._lib import DtaError  # noqa: F401
 
-__all__ = ["attn_fwd", "attn_merge", "residual_diff", "fp8_quant_per_tensor",
+__all__ = ["attn_fwd", "attn_merge", "attn_fwd_accum", "attn_merge_into", "residual_diff",
+           "fp8_quant_per_tensor",
            "attn_fwd_fp8", "workspace", "DtaError"]
 
 _workspaces = {}
@@ -109,6 +110,43 @@ def attn_merge(o_parts, lse_parts, o=None, lse=None):
     st = _lib.lib().attn_merge(_ptr(o_parts), _ptr(lse_parts), n, _ptr(o), _ptr(lse),
                                B, H, Nq, D, ctypes_ptr(_stream(o_parts)))
     _lib.check("attn_merge", st)
+    return o, lse
+
+
+def attn_fwd_accum(q, k, v, o, lse, scale=None):
+    """One ring step fused: fold the attention of q over this k/v chunk into the
+    running (o bf16 [B,H,Nq,D], lse f32 [B,H,Nq]) in place; returns (o, lse)."""
+    _need(q, "q", torch.bfloat16, 4)
+    _need(k, "k", torch.bfloat16, 4)
+    _need(v, "v", torch.bfloat16, 4)
+    _need(o, "o", torch.bfloat16, 4)
+    _need(lse, "lse", torch.float32, 3)
+    B, H, Nq, D = q.shape
+    Nkv = k.shape[2]
+    if tuple(k.shape) != (B, H, Nkv, D) or tuple(v.shape) != (B, H, Nkv, D):
+        raise ValueError("shape mismatch: q %s k %s v %s" % (tuple(q.shape), tuple(k.shape), tuple(v.shape)))
+    if o.shape != q.shape or tuple(lse.shape) != (B, H, Nq):
+        raise ValueError("o must have q's shape and lse must be [B,H,Nq]")
+    if scale is None:
+        scale = D ** -0.5
+    st = _lib.lib().attn_fwd_accum(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                   B, H, Nq, Nkv, D, float(scale), ctypes_ptr(_stream(q)))
+    _lib.check("attn_fwd_accum", st)
+    return o, lse
+
+
+def attn_merge_into(o, lse, o_part, lse_part):
+    """(o, lse) <- merge((o, lse), (o_part, lse_part)) in place; returns (o, lse)."""
+    _need(o, "o", torch.bfloat16, 4)
+    _need(lse, "lse", torch.float32, 3)
+    _need(o_part, "o_part", torch.bfloat16, 4)
+    _need(lse_part, "lse_part", torch.float32, 3)
+    B, H, Nq, D = o.shape
+    if o_part.shape != o.shape or lse.shape != lse_part.shape or tuple(lse.shape) != (B, H, Nq):
+        raise ValueError("o/o_part must match and lse/lse_part must be [B,H,Nq]")
+    st = _lib.lib().attn_merge_into(_ptr(o), _ptr(lse), _ptr(o_part), _ptr(lse_part),
+                                    B, H, Nq, D, ctypes_ptr(_stream(o)))
+    _lib.check("attn_merge_into", st)
     return o, lse
 
 

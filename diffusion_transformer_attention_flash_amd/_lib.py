@@ -19,6 +19,8 @@ _F = ctypes.c_float
 SIGNATURES = {
     "attn_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P]),
     "attn_merge": (_I, [_P, _P, _I, _P, _P, _I, _I, _I, _I, _P]),
+    "attn_fwd_accum": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P]),
+    "attn_merge_into": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _P]),
     "residual_diff": (_I, [_P, _P, _I64, _P, _P, _P]),
     "fp8_quant_per_tensor": (_I, [_P, _I64, _P, _P, _P, _P]),
     "attn_fwd_fp8": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P]),

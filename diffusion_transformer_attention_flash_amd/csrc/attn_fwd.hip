@@ -81,7 +81,9 @@ __device__ __forceinline__ float xhalf_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int D, int NW, int BN>
+// ACCUM: instead of writing this K/V chunk's (O, LSE), merge it into the
+// running (O, LSE) already in o / lse (one ring-attention step, fused).
+template <int D, int NW, int BN, bool ACCUM>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
@@ -265,9 +267,11 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_bf16_kernel(
 
   // Epilogue: lane owns query `row` and dims db*32 + 8*(r/4) + 4g + r%4.
   const float lt = xhalf_sum(l_run);
-  const float inv = 1.0f / lt;
-  if (row < Nq) {
-    uint16_t* orow = o + q_base + (int64_t)row * D;
+  if (row >= Nq) return;
+  uint16_t* orow = o + q_base + (int64_t)row * D;
+  const int64_t li = (int64_t)bh * Nq + row;
+  if constexpr (!ACCUM) {
+    const float inv = 1.0f / lt;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -277,12 +281,46 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_bf16_kernel(
                    pack_bf16x2(a[4 * jj + 2] * inv, a[4 * jj + 3] * inv)};
         *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * jj + 4 * g) = w;
       }
-    if (g == 0 && lse != nullptr)
-      lse[(int64_t)bh * Nq + row] = (m_run + log2f(lt)) * kLn2;
+    if (g == 0 && lse != nullptr) lse[li] = (m_run + log2f(lt)) * kLn2;
+  } else {
+    // Two-part log-sum-exp merge in the log2 domain: the running part (O_r,
+    // L_r) from memory and this chunk's (acc / lt, m_run + log2 lt). A running
+    // L_r of -inf means "nothing seen yet": weight 0, and O_r is not used.
+    const float lc = m_run + log2f(lt);
+    const float lr = lse[li] * kLog2e;
+    const float mm = fmaxf(lc, lr);
+    const float wr = __builtin_amdgcn_exp2f(lr - mm);
+    const float wc = __builtin_amdgcn_exp2f(lc - mm);
+    const float den = wr + wc;
+    const float ar = wr / den;
+    const float ac = wc / (den * lt);
+    const bool use_r = wr > 0.f;
+    u32x2 prev[D / 32][4];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        prev[db][jj] = *reinterpret_cast<const u32x2*>(orow + db * 32 + 8 * jj + 4 * g);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const f32x16& a = oacc[db];
+        float x[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t wv = prev[db][jj][e >> 1];
+          const float orv = bf16_bits_to_f32((e & 1) ? (wv >> 16) : (wv & 0xFFFF));
+          x[e] = a[4 * jj + e] * ac + (use_r ? orv * ar : 0.f);
+        }
+        const u32x2 w = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+        *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * jj + 4 * g) = w;
+      }
+    if (g == 0) lse[li] = (mm + log2f(den)) * kLn2;
   }
 }
 
-template <int D, int NW, int BN>
+template <int D, int NW, int BN, bool ACCUM>
 static int launch_attn_fwd(const void* q, const void* k, const void* v,
                            void* o, float* lse, int B, int H, int Nq, int Nkv,
                            float scale, hipStream_t stream) {
@@ -290,7 +328,7 @@ static int launch_attn_fwd(const void* q, const void* k, const void* v,
   const int n_qt = (Nq + C::kBM - 1) / C::kBM;
   const int64_t grid = (int64_t)n_qt * B * H;
   if (grid > 0x7FFFFFFF) return DTA_EUNSUPPORTED;
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, NW, BN>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, NW, BN, ACCUM>), dim3((unsigned)grid),
                      dim3(C::kThreads), 0, stream,
                      static_cast<const uint16_t*>(q),
                      static_cast<const uint16_t*>(k),
@@ -307,9 +345,10 @@ static bool aligned(const void* p, uintptr_t a) {
   return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0;
 }
 
-extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o,
-                        float* lse, int B, int H, int Nq, int Nkv, int D,
-                        float scale, hipStream_t stream) {
+// Argument checks shared by attn_fwd and attn_fwd_accum.
+static int check_attn_args(const void* q, const void* k, const void* v, const void* o,
+                           const float* lse, int B, int H, int Nq, int Nkv, int D,
+                           float scale) {
   if (!q || !k || !v || !o) return DTA_EINVAL;
   if (B < 1 || H < 1 || Nq < 1 || Nkv < 1) return DTA_EINVAL;
   if (!(scale >= 0.f) || !__builtin_isfinite(scale)) return DTA_EINVAL;
@@ -317,7 +356,26 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o,
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
       (lse && !aligned(lse, 4)))
     return DTA_EALIGN;
+  return DTA_OK;
+}
+
+extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o,
+                        float* lse, int B, int H, int Nq, int Nkv, int D,
+                        float scale, hipStream_t stream) {
+  const int st = check_attn_args(q, k, v, o, lse, B, H, Nq, Nkv, D, scale);
+  if (st != DTA_OK) return st;
   if (D == 128)
-    return launch_attn_fwd<128, 8, 64>(q, k, v, o, lse, B, H, Nq, Nkv, scale, stream);
-  return launch_attn_fwd<64, 4, 64>(q, k, v, o, lse, B, H, Nq, Nkv, scale, stream);
+    return launch_attn_fwd<128, 8, 64, false>(q, k, v, o, lse, B, H, Nq, Nkv, scale, stream);
+  return launch_attn_fwd<64, 4, 64, false>(q, k, v, o, lse, B, H, Nq, Nkv, scale, stream);
+}
+
+extern "C" int attn_fwd_accum(const void* q, const void* k, const void* v, void* o,
+                              float* lse, int B, int H, int Nq, int Nkv, int D,
+                              float scale, hipStream_t stream) {
+  if (!lse) return DTA_EINVAL;
+  const int st = check_attn_args(q, k, v, o, lse, B, H, Nq, Nkv, D, scale);
+  if (st != DTA_OK) return st;
+  if (D == 128)
+    return launch_attn_fwd<128, 8, 64, true>(q, k, v, o, lse, B, H, Nq, Nkv, scale, stream);
+  return launch_attn_fwd<64, 4, 64, true>(q, k, v, o, lse, B, H, Nq, Nkv, scale, stream);
 }

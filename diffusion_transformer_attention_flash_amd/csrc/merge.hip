@@ -10,6 +10,7 @@
 // so every load and store is a coalesced 128-bit access; the per-row LSE
 // values are read by the D/8 threads of the row and served by one cache line.
 // Partials are visited four at a time so that several loads are in flight.
+// attn_merge_into is the two-part, in-place form used after each ring step.
 
 #include "common.h"
 
@@ -46,10 +47,13 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           wsum += w[u];
+          const bool live = w[u] > 0.f;   // a weight-0 partial's O is never used
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            acc[2 * e] = fmaf(w[u], bf16_bits_to_f32(x[u][e] & 0xFFFF), acc[2 * e]);
-            acc[2 * e + 1] = fmaf(w[u], bf16_bits_to_f32(x[u][e] >> 16), acc[2 * e + 1]);
+            const float a0 = fmaf(w[u], bf16_bits_to_f32(x[u][e] & 0xFFFF), acc[2 * e]);
+            const float a1 = fmaf(w[u], bf16_bits_to_f32(x[u][e] >> 16), acc[2 * e + 1]);
+            acc[2 * e] = live ? a0 : acc[2 * e];
+            acc[2 * e + 1] = live ? a1 : acc[2 * e + 1];
           }
         }
       }
@@ -59,10 +63,13 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(
         const float w = __builtin_amdgcn_exp2f(
             fmaf(lp[(int64_t)p * rows + row], kLog2e, -ml2));
         wsum += w;
+        const bool live = w > 0.f;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          acc[2 * e] = fmaf(w, bf16_bits_to_f32(x[e] & 0xFFFF), acc[2 * e]);
-          acc[2 * e + 1] = fmaf(w, bf16_bits_to_f32(x[e] >> 16), acc[2 * e + 1]);
+          const float a0 = fmaf(w, bf16_bits_to_f32(x[e] & 0xFFFF), acc[2 * e]);
+          const float a1 = fmaf(w, bf16_bits_to_f32(x[e] >> 16), acc[2 * e + 1]);
+          acc[2 * e] = live ? a0 : acc[2 * e];
+          acc[2 * e + 1] = live ? a1 : acc[2 * e + 1];
         }
       }
       const float inv = 1.0f / wsum;
@@ -75,6 +82,51 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(
     *reinterpret_cast<u32x4*>(o + row * D + ch * 8) = out;
     if (ch == 0 && lse != nullptr)
       lse[row] = (m == -INFINITY) ? -INFINITY : m + logf(wsum);
+  }
+}
+
+// (o, lse) <- merge((o, lse), (op, lp)), in place. The D/8 threads of a row
+// are consecutive lanes of one wave, so every lane of the row reads lse[row]
+// before the row's first lane overwrites it.
+template <int D>
+__global__ __launch_bounds__(256) void attn_merge_into_kernel(
+    uint16_t* __restrict__ o, float* __restrict__ lse, const uint16_t* __restrict__ op,
+    const float* __restrict__ lp, int64_t rows) {
+  constexpr int kCh = D / 8;
+  static_assert(64 % kCh == 0, "a row must not straddle two waves");
+  const int64_t total = rows * kCh;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t ci = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; ci < total;
+       ci += stride) {
+    const int64_t row = ci / kCh;
+    const int ch = (int)(ci - row * kCh);
+    const float la = lse[row], lb = lp[row];
+    const u32x4 xa = *reinterpret_cast<const u32x4*>(o + row * D + ch * 8);
+    const u32x4 xb = *reinterpret_cast<const u32x4*>(op + row * D + ch * 8);
+    const float m = fmaxf(la, lb);
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float lout = -INFINITY;
+    if (m != -INFINITY) {
+      const float ml2 = m * kLog2e;
+      const float wa = __builtin_amdgcn_exp2f(fmaf(la, kLog2e, -ml2));
+      const float wb = __builtin_amdgcn_exp2f(fmaf(lb, kLog2e, -ml2));
+      const float inv = 1.0f / (wa + wb);
+      const float fa = wa * inv, fb = wb * inv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        // A part of weight 0 contributes nothing, whatever its O holds.
+        const float a0 = bf16_bits_to_f32(xa[e] & 0xFFFF), a1 = bf16_bits_to_f32(xa[e] >> 16);
+        const float b0 = bf16_bits_to_f32(xb[e] & 0xFFFF), b1 = bf16_bits_to_f32(xb[e] >> 16);
+        acc[2 * e] = (wa > 0.f ? fa * a0 : 0.f) + (wb > 0.f ? fb * b0 : 0.f);
+        acc[2 * e + 1] = (wa > 0.f ? fa * a1 : 0.f) + (wb > 0.f ? fb * b1 : 0.f);
+      }
+      lout = m + logf(wa + wb);
+    }
+    u32x4 out;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) out[e] = pack_bf16x2(acc[2 * e], acc[2 * e + 1]);
+    *reinterpret_cast<u32x4*>(o + row * D + ch * 8) = out;
+    if (ch == 0) lse[row] = lout;
   }
 }
 
@@ -105,5 +157,30 @@ extern "C" int attn_merge(const void* o_parts, const float* lse_parts,
     hipLaunchKernelGGL(attn_merge_kernel<64>, dim3(grid), dim3(256), 0, stream,
                        static_cast<const uint16_t*>(o_parts), lse_parts, n_parts,
                        static_cast<uint16_t*>(o), lse, rows);
+  return hipGetLastError() == hipSuccess ? DTA_OK : DTA_ELAUNCH;
+}
+
+extern "C" int attn_merge_into(void* o, float* lse, const void* o_part,
+                               const float* lse_part, int B, int H, int Nq, int D,
+                               hipStream_t stream) {
+  if (!o || !lse || !o_part || !lse_part) return DTA_EINVAL;
+  if (B < 1 || H < 1 || Nq < 1) return DTA_EINVAL;
+  if (D != 64 && D != 128) return DTA_EUNSUPPORTED;
+  auto al = [](const void* p, uintptr_t a) {
+    return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0;
+  };
+  if (!al(o, 16) || !al(o_part, 16) || !al(lse, 4) || !al(lse_part, 4)) return DTA_EALIGN;
+  const int64_t rows = (int64_t)B * H * Nq;
+  const int64_t total = rows * (D / 8);
+  const int64_t want = (total + 255) / 256;
+  const unsigned grid = (unsigned)(want < 65536 ? want : 65536);
+  if (D == 128)
+    hipLaunchKernelGGL(attn_merge_into_kernel<128>, dim3(grid), dim3(256), 0, stream,
+                       static_cast<uint16_t*>(o), lse, static_cast<const uint16_t*>(o_part),
+                       lse_part, rows);
+  else
+    hipLaunchKernelGGL(attn_merge_into_kernel<64>, dim3(grid), dim3(256), 0, stream,
+                       static_cast<uint16_t*>(o), lse, static_cast<const uint16_t*>(o_part),
+                       lse_part, rows);
   return hipGetLastError() == hipSuccess ? DTA_OK : DTA_ELAUNCH;
 }

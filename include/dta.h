@@ -84,6 +84,52 @@ int attn_merge(const void* o_parts, const float* lse_parts, int n_parts,
                hipStream_t stream);
 
 /*
+ * attn_fwd_accum -- one ring-attention step with the merge fused into the
+ * attention epilogue (diffusers "Context parallelism" guide, section "Ring
+ * Attention": each rank folds every K/V block it receives into its running
+ * output). With (O_r, L_r) the running state held in o / lse and (O_c, L_c)
+ * what attn_fwd would return for this K/V chunk, o / lse are overwritten in
+ * place with the two-part attn_merge of the pair:
+ *     M = max(L_r, L_c);  w_r = exp(L_r - M), w_c = exp(L_c - M)
+ *     O = (w_r O_r + w_c O_c) / (w_r + w_c);  LSE = M + ln(w_r + w_c)
+ * O_c is never rounded: the merge takes the float32 accumulator; only the
+ * merged O is rounded to bf16, once per call (so a ring of n steps rounds the
+ * running O n times, where attn_fwd + attn_merge round each partial once and
+ * the merged O once). A row with L_r = -inf is "nothing seen yet": its O_r is
+ * ignored (it may hold anything, NaN included) and the row receives the
+ * chunk's result. Typical use: the first step calls attn_fwd (or starts from
+ * lse filled with -inf), later steps call attn_fwd_accum on the same o / lse.
+ * Steps on one (o, lse) must be ordered (one stream).
+ *
+ * q, k, v, B, H, Nq, Nkv, D, scale   as attn_fwd
+ * o     bf16 [B,H,Nq,D], 16-byte aligned, read and written
+ * lse   float [B,H,Nq], 4-byte aligned, read and written; must not be NULL;
+ *       entries finite or -inf
+ * Returns DTA_OK, DTA_EINVAL, DTA_EUNSUPPORTED, DTA_EALIGN or DTA_ELAUNCH.
+ */
+int attn_fwd_accum(const void* q, const void* k, const void* v, void* o,
+                   float* lse, int B, int H, int Nq, int Nkv, int D,
+                   float scale, hipStream_t stream);
+
+/*
+ * attn_merge_into -- the pairwise, in-place form of attn_merge, for a
+ * partial that arrives already computed (same guide and section):
+ *     (o, lse) <- attn_merge of {(o, lse), (o_part, lse_part)}
+ * A part with LSE = -inf gets zero weight and its O is ignored; a row whose
+ * two LSEs are both -inf gets O = 0 and LSE = -inf. Arithmetic is float32,
+ * the result is rounded to bf16 once.
+ *
+ * o         bf16 [B,H,Nq,D], 16-byte aligned, read and written
+ * lse       float [B,H,Nq], 4-byte aligned, read and written (not NULL)
+ * o_part    bf16 [B,H,Nq,D], 16-byte aligned (must not alias o)
+ * lse_part  float [B,H,Nq], 4-byte aligned (not NULL)
+ * B,H,Nq >= 1; D in {64, 128}.
+ */
+int attn_merge_into(void* o, float* lse, const void* o_part,
+                    const float* lse_part, int B, int H, int Nq, int D,
+                    hipStream_t stream);
+
+/*
  * residual_diff -- First Block Cache's relative residual difference
  * (ParaAttention guide, section "First Block Cache"):
  *     out = sum_k |a_k - b_k| / sum_k |b_k|  ( = mean|a-b| / mean|b| )

@@ -70,6 +70,27 @@ def test_attn_merge_validation():
     assert f(ODD, GOOD, 2, GOOD, GOOD, 1, 1, 1, 128, None) == _lib.DTA_EALIGN
 
 
+def test_attn_fwd_accum_validation():
+    f = _lib.lib().attn_fwd_accum
+    ok = (GOOD, GOOD, GOOD, GOOD, GOOD)
+    assert f(GOOD, GOOD, GOOD, GOOD, None, 1, 1, 1, 1, 128, 0.1, None) == _lib.DTA_EINVAL  # lse required
+    assert f(None, GOOD, GOOD, GOOD, GOOD, 1, 1, 1, 1, 128, 0.1, None) == _lib.DTA_EINVAL
+    assert f(*ok, 1, 1, 1, 0, 128, 0.1, None) == _lib.DTA_EINVAL
+    assert f(*ok, 1, 1, 1, 1, 128, -1.0, None) == _lib.DTA_EINVAL
+    assert f(*ok, 1, 1, 1, 1, 96, 0.1, None) == _lib.DTA_EUNSUPPORTED
+    assert f(GOOD, GOOD, GOOD, ODD, GOOD, 1, 1, 1, 1, 128, 0.1, None) == _lib.DTA_EALIGN
+    assert f(GOOD, GOOD, GOOD, GOOD, ctypes.c_void_p(0x10002), 1, 1, 1, 1, 64, 0.1, None) == _lib.DTA_EALIGN
+
+
+def test_attn_merge_into_validation():
+    f = _lib.lib().attn_merge_into
+    assert f(GOOD, None, GOOD, GOOD, 1, 1, 1, 128, None) == _lib.DTA_EINVAL
+    assert f(GOOD, GOOD, GOOD, None, 1, 1, 1, 128, None) == _lib.DTA_EINVAL
+    assert f(GOOD, GOOD, GOOD, GOOD, 1, 0, 1, 128, None) == _lib.DTA_EINVAL
+    assert f(GOOD, GOOD, GOOD, GOOD, 1, 1, 1, 48, None) == _lib.DTA_EUNSUPPORTED
+    assert f(GOOD, GOOD, ODD, GOOD, 1, 1, 1, 128, None) == _lib.DTA_EALIGN
+
+
 def test_reductions_validation():
     lib = _lib.lib()
     assert lib.residual_diff(GOOD, GOOD, 0, GOOD, GOOD, None) == _lib.DTA_EINVAL
