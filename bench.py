@@ -248,6 +248,46 @@ def main():
                "residual": "residual_diff"}
     legs = {leg_key[x]: legs[leg_key[x]] for x in leg_key if x in legs_on}
 
+    # The HBM-bound kernels once more, each alone and cold: a 512 MB read
+    # between repetitions evicts the 256 MB MALL (a read, so that no dirty
+    # lines are left to write back during the timed kernel). A device copy of
+    # the same byte count gives the bandwidth reachable at these sizes.
+    flush = torch.ones(128 << 20, dtype=torch.float32, device=dev)
+    fsum = torch.empty((1,), dtype=torch.float32, device=dev)
+
+    def cold_us(fn, reps=20):
+        ts = []
+        for r in range(reps + 2):
+            torch.sum(flush, dim=(0,), out=fsum[0])
+            a_ev, b_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a_ev.record()
+            fn()
+            b_ev.record()
+            torch.cuda.synchronize()
+            if r >= 2:
+                ts.append(a_ev.elapsed_time(b_ev) * 1e3)
+        ts.sort()
+        return ts[len(ts) // 2], ts[0]
+
+    cold = {}
+    if "merge" in legs_on:
+        cold["attn_merge"] = (lambda: dta.attn_merge(o_parts, l_parts, o=o_m, lse=l_m), merge_bytes)
+    if "quant" in legs_on:
+        cold["fp8_quant_q"] = (lambda: dta.fp8_quant_per_tensor(q, q8, ds[0:1]), quant_bytes // 3)
+    if "residual" in legs_on:
+        cold["residual_diff"] = (lambda: dta.residual_diff(ra, rb, out=rd), res_bytes)
+    if cold:
+        cp_dst = torch.empty_like(ra)
+        cold["device_copy_same_bytes_as_residual"] = (lambda: cp_dst.copy_(ra), res_bytes)
+        for name, (fn, nbytes) in cold.items():
+            med, mn = cold_us(fn)
+            legs.setdefault("cold", {})[name] = {
+                "us_median": med, "us_min": mn, "bytes": nbytes,
+                "GB/s_median": nbytes / (med * 1e-6) / 1e9,
+                "frac_hbm_peak": nbytes / (med * 1e-6) / 1e9 / PEAK_HBM_GBS}
+        del cp_dst
+    del flush
+
     # The same ring with the merge fused into each step (attn_fwd_accum): the
     # first chunk by attn_fwd, the other seven folded into one running (o, lse).
     # Timed apart from the step, which keeps the separate partials + merge.
