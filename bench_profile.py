@@ -55,9 +55,10 @@ def _col(row, *keys):
 
 def cmd_summarize_trace(args):
     """Per-kernel statistics from the kernel trace. Launches of one kernel
-    that follow each other directly form a run; the first launch of a run is
-    reported apart from the rest (bench.py's step launches the full-K/V
-    attention first, then the 8 chunk attentions with the same grid)."""
+    that follow each other directly form a run; launches are grouped by run
+    length and by whether they open the run (bench.py's step launches the
+    full-K/V attention first, then the 8 chunk attentions with the same grid:
+    a run of 9 whose first launch is the full attention)."""
     rows = []
     for path in _find(args.dir, "kernel_trace.csv"):
         with open(path) as f:
@@ -65,16 +66,23 @@ def cmd_summarize_trace(args):
     if not rows:
         raise SystemExit("empty trace")
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
-    groups = {}
-    prev = None
-    pos = 0
+    # Runs: maximal sequences of consecutive launches of one kernel. A launch
+    # is labelled by its run's length and whether it opens the run.
+    runs, cur = [], []
     for r in rows:
-        name = r["Kernel_Name"]
-        pos = pos + 1 if name == prev else 0
-        prev = name
-        grid = r.get("Grid_Size_X") or r.get("Grid_Size") or "?"
-        key = (name, grid, "first of run" if pos == 0 else "later in run")
-        groups.setdefault(key, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+        if cur and r["Kernel_Name"] != cur[-1]["Kernel_Name"]:
+            runs.append(cur)
+            cur = []
+        cur.append(r)
+    if cur:
+        runs.append(cur)
+    groups = {}
+    for run in runs:
+        for pos, r in enumerate(run):
+            grid = r.get("Grid_Size_X") or r.get("Grid_Size") or "?"
+            where = ("first of run of %d" if pos == 0 else "later in run of %d") % len(run)
+            key = (r["Kernel_Name"], grid, where)
+            groups.setdefault(key, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
     lines = ["# rocprofv3 kernel trace: %s" % args.title, "",
              "Command (repo root): `%s`" % args.cmd, "",
              "| kernel | grid (threads) | launches | calls | average (us) | median (us) | total (ms) |",
