@@ -399,3 +399,87 @@ def test_fp8_attention_close_to_dequantised_attention():
     assert np.abs(o8 - o).max() <= bound
     # and it is a genuine (if small) perturbation, not a no-op
     assert np.abs(o8 - o).max() > 0
+
+
+# ---- First Block Cache decision + apply (fbcache_step) --------------------
+
+def _bf16_candidates_nearest(x):
+    """Brute force: the bfloat16 nearest to the Fraction x, ties to even, by
+    scanning the two representable neighbours built from float32 bit patterns."""
+    from fractions import Fraction
+    import struct
+    f = float(x)                                   # nearest double, a start point
+    bits = struct.unpack("<I", struct.pack("<f", np.float32(f)))[0] & 0xFFFF0000
+    best = None
+    for b in (bits - 0x10000, bits, bits + 0x10000, bits + 0x20000):
+        b &= 0xFFFFFFFF
+        v = struct.unpack("<f", struct.pack("<I", b))[0]
+        if not np.isfinite(v):
+            continue
+        d = abs(Fraction(v) - x)
+        key = (d, (b >> 16) & 1)                   # nearest, then even mantissa
+        if best is None or key < best[0]:
+            best = (key, v)
+    return best[1]
+
+
+def test_fbcache_bf16_round_matches_torch_from_float32():
+    from oracle.residual import _bf16_round
+    g = np.random.default_rng(11)
+    x = np.concatenate([g.standard_normal(4000) * 10.0 ** g.integers(-30, 30, 4000),
+                        [0.0, -0.0, 1.0, 3.0e38, -3.0e38, 1e-39, -1e-40]]).astype(np.float32)
+    want = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    got = _bf16_round(x.astype(np.float64))
+    assert np.array_equal(got, want)
+
+
+def test_fbcache_sum_is_correctly_rounded():
+    """hidden + cached rounded once equals the brute-force nearest bfloat16 of
+    the exact rational sum (including ties and wide exponent gaps)."""
+    from fractions import Fraction
+    from oracle.residual import _bf16_round
+    g = np.random.default_rng(12)
+    h = torch.from_numpy(g.standard_normal(600).astype(np.float32) *
+                         (2.0 ** g.integers(-20, 20, 600)).astype(np.float32)).to(torch.bfloat16)
+    c = torch.from_numpy(g.standard_normal(600).astype(np.float32) *
+                         (2.0 ** g.integers(-20, 20, 600)).astype(np.float32)).to(torch.bfloat16)
+    # exact ties: h = 1 + 2^-7 (odd last bit) plus 2^-8 (half an ulp)
+    h[0] = 1.0 + 2.0 ** -7
+    c[0] = 2.0 ** -8
+    h[1] = 1.0
+    c[1] = 2.0 ** -8
+    hf, cf = h.double().numpy(), c.double().numpy()
+    got = _bf16_round(hf + cf)
+    for i in range(len(hf)):
+        want = _bf16_candidates_nearest(Fraction(hf[i]) + Fraction(cf[i]))
+        assert got[i] == want, (i, hf[i], cf[i], got[i], want)
+    assert got[0] == 1.0 + 2.0 ** -6 and got[1] == 1.0          # ties to even
+
+
+def test_fbcache_decision_closed_forms():
+    b = torch.tensor([1.0, -2.0, 0.5, 4.0]).to(torch.bfloat16)
+    h = torch.tensor([1.0, 2.0, 3.0, 4.0]).to(torch.bfloat16)
+    c = torch.tensor([0.5, -1.0, 0.25, 8.0]).to(torch.bfloat16)
+    # r = 2 b -> diff exactly 1
+    for thr, use in ((1.5, True), (1.0, False), (0.5, False)):
+        d, u, out = oracle.fbcache_step(2 * b, b, thr, h, c)
+        assert d == 1.0 and u is use
+        assert np.array_equal(out, [1.5, 1.0, 3.25, 12.0] if use else [1.0, 2.0, 3.0, 4.0])
+    # identical residuals: diff 0, and 0 < 0 is false
+    assert oracle.fbcache_step(b, b, 0.0, h, c)[1] is False
+    assert oracle.fbcache_step(b, b, 1e-30, h, c)[1] is True
+    # previous residual all zero: inf or NaN never reuses
+    z = torch.zeros(4, dtype=torch.bfloat16)
+    assert oracle.fbcache_step(b, z, 1e30, h, c)[1] is False       # x / 0 = inf
+    assert oracle.fbcache_step(z, z, 1e30, h, c)[1] is False       # 0 / 0 = NaN
+
+
+def test_fbcache_decision_is_taken_in_float32():
+    # diff = 1/3 in float64; float32(1/3) = 0.3333333432674408 > 1/3
+    b = torch.tensor([3.0]).to(torch.bfloat16)
+    a = torch.tensor([4.0]).to(torch.bfloat16)
+    h = torch.tensor([1.0]).to(torch.bfloat16)
+    d, use, _ = oracle.fbcache_step(a, b, float(np.float32(1.0 / 3.0)), h, h)
+    assert d == 1.0 / 3.0 and use is False        # equal in float32: not below
+    d, use, _ = oracle.fbcache_step(a, b, float(np.nextafter(np.float32(1.0 / 3.0), np.float32(1))), h, h)
+    assert use is True
