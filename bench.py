@@ -288,6 +288,34 @@ def main():
         del cp_dst
     del flush
 
+    # First Block Cache step on the device (residual_diff + decision + the
+    # guarded hidden += cached) at the FLUX residual shape, once with a
+    # threshold that reuses the cache and once with one that does not.
+    if "residual" in legs_on:
+        hid = torch.zeros_like(ra)
+        cac = torch.full_like(ra, 2.0 ** -9)
+        fd = torch.empty((), dtype=torch.float32, device=dev)
+        fu = torch.empty((), dtype=torch.int32, device=dev)
+        fb = {}
+        for label, thr in (("reuse", 1.0), ("recompute", 0.0)):
+            fn = (lambda t: (lambda: dta.fbcache_step(ra, rb, t, hid, cac, diff=fd, use_cache=fu)))(thr)
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(args.steps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) / args.steps * 1e3
+            nbytes = res_bytes + (3 * ra.numel() * 2 if label == "reuse" else 0)
+            fb[label] = {"us": us, "use_cache": int(fu.item()), "bytes": nbytes,
+                         "GB/s": nbytes / (us * 1e-6) / 1e9}
+        fb["in_step"] = False
+        legs["fbcache_step"] = fb
+        del hid, cac
+
     # The same ring with the merge fused into each step (attn_fwd_accum): the
     # first chunk by attn_fwd, the other seven folded into one running (o, lse).
     # Timed apart from the step, which keeps the separate partials + merge.

@@ -19,6 +19,7 @@ from . import _lib
 from ._lib import DtaError  # noqa: F401
 
 __all__ = ["attn_fwd", "attn_merge", "attn_fwd_accum", "attn_merge_into", "residual_diff",
+           "fbcache_step",
            "fp8_quant_per_tensor",
            "attn_fwd_fp8", "workspace", "DtaError"]
 
@@ -165,6 +166,30 @@ def residual_diff(a, b, out=None):
                                   ctypes_ptr(_stream(a)))
     _lib.check("residual_diff", st)
     return out
+
+
+def fbcache_step(r, r_prev, threshold, hidden, cached, diff=None, use_cache=None):
+    """First Block Cache step on the device: diff = residual_diff(r, r_prev),
+    use = diff < threshold, and hidden += cached (in place) when use.
+    Returns (diff f32 scalar, use_cache int32 scalar), both device tensors."""
+    _need(r, "r", torch.bfloat16)
+    _need(r_prev, "r_prev", torch.bfloat16)
+    _need(hidden, "hidden", torch.bfloat16)
+    _need(cached, "cached", torch.bfloat16)
+    if r.numel() != r_prev.numel():
+        raise ValueError("r and r_prev must have the same number of elements")
+    if hidden.numel() != cached.numel():
+        raise ValueError("hidden and cached must have the same number of elements")
+    if diff is None:
+        diff = torch.empty((), dtype=torch.float32, device=r.device)
+    if use_cache is None:
+        use_cache = torch.empty((), dtype=torch.int32, device=r.device)
+    ws = workspace(r.device)
+    st = _lib.lib().fbcache_step(_ptr(r), _ptr(r_prev), r.numel(), float(threshold),
+                                 _ptr(hidden), _ptr(cached), hidden.numel(), _ptr(diff),
+                                 _ptr(use_cache), _ptr(ws), ctypes_ptr(_stream(r)))
+    _lib.check("fbcache_step", st)
+    return diff, use_cache
 
 
 def fp8_quant_per_tensor(x, x8=None, descale=None):

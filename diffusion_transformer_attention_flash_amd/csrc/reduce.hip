@@ -1,6 +1,8 @@
 // Grid-wide reductions over bf16 tensors:
 // * residual_diff -- First Block Cache's relative residual difference
 //   sum|a-b| / sum|b| (ParaAttention guide, section "First Block Cache").
+// * fbcache_step -- the same reduction, the cache decision diff < threshold
+//   into a device flag, and the flag-guarded apply hidden += cached.
 // * fp8_quant_per_tensor -- per-tensor dynamic E4M3FN quantisation, scale
 //   amax|x|/448 (ParaAttention guide, section "fp8 quantization").
 //
@@ -101,6 +103,61 @@ __global__ __launch_bounds__(256) void residual_diff_finish_kernel(
     __syncthreads();
   }
   if (threadIdx.x == 0) *out = (float)(fx[0] / fy[0]);
+}
+
+// First Block Cache: the same fixed-order finish, then the decision
+// diff < threshold (float32; a NaN diff or threshold gives 0) into a device
+// flag that the apply kernel reads -- no host round trip.
+__global__ __launch_bounds__(256) void fbcache_finish_kernel(
+    const double* __restrict__ part, float threshold, float* __restrict__ diff,
+    int* __restrict__ use_cache) {
+  __shared__ double fx[256], fy[256];
+  double x = 0.0, y = 0.0;
+  for (int p = threadIdx.x; p < kRedBlocks; p += 256) {
+    x += part[2 * p];
+    y += part[2 * p + 1];
+  }
+  fx[threadIdx.x] = x;
+  fy[threadIdx.x] = y;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (threadIdx.x < s) {
+      fx[threadIdx.x] += fx[threadIdx.x + s];
+      fy[threadIdx.x] += fy[threadIdx.x + s];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const float d = (float)(fx[0] / fy[0]);
+    *diff = d;
+    *use_cache = (d < threshold) ? 1 : 0;
+  }
+}
+
+// hidden += cached (float32 sum of two bf16, rounded once to bf16) when the
+// flag is set; every workgroup leaves at once otherwise.
+__global__ __launch_bounds__(256) void fbcache_apply_kernel(
+    uint16_t* __restrict__ hidden, const uint16_t* __restrict__ cached, int64_t n,
+    const int* __restrict__ use_cache) {
+  if (*use_cache == 0) return;
+  const int64_t n8 = n >> 3;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  u32x4* h4 = reinterpret_cast<u32x4*>(hidden);
+  const u32x4* c4 = reinterpret_cast<const u32x4*>(cached);
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += stride) {
+    const u32x4 h = h4[i], c = c4[i];
+    u32x4 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      r[e] = pack_bf16x2(bf16_bits_to_f32(h[e] & 0xFFFF) + bf16_bits_to_f32(c[e] & 0xFFFF),
+                         bf16_bits_to_f32(h[e] >> 16) + bf16_bits_to_f32(c[e] >> 16));
+    h4[i] = r;
+  }
+  if (blockIdx.x == 0 && threadIdx.x < (n & 7)) {
+    const int64_t t = (n8 << 3) + threadIdx.x;
+    const float v = bf16_bits_to_f32(hidden[t]) + bf16_bits_to_f32(cached[t]);
+    hidden[t] = (uint16_t)(pack_bf16x2(v, 0.f) & 0xFFFF);
+  }
 }
 
 // |x| maximum over bf16 bit patterns: for non-NaN values the order of the
@@ -211,6 +268,30 @@ extern "C" int residual_diff(const void* a, const void* b, int64_t n, float* out
                      n, part);
   if (hipGetLastError() != hipSuccess) return DTA_ELAUNCH;
   hipLaunchKernelGGL(residual_diff_finish_kernel, dim3(1), dim3(256), 0, stream, part, out);
+  return hipGetLastError() == hipSuccess ? DTA_OK : DTA_ELAUNCH;
+}
+
+extern "C" int fbcache_step(const void* r, const void* r_prev, int64_t n, float threshold,
+                            void* hidden, const void* cached, int64_t n_hidden,
+                            float* diff, int* use_cache, void* ws, hipStream_t stream) {
+  if (!r || !r_prev || !hidden || !cached || !diff || !use_cache || !ws) return DTA_EINVAL;
+  if (n < 1 || n_hidden < 1) return DTA_EINVAL;
+  if (!al16(r) || !al16(r_prev) || !al16(hidden) || !al16(cached) || !al16(ws) ||
+      (reinterpret_cast<uintptr_t>(diff) & 3) || (reinterpret_cast<uintptr_t>(use_cache) & 3))
+    return DTA_EALIGN;
+  double* part = static_cast<double*>(ws);
+  hipLaunchKernelGGL(residual_diff_kernel, dim3(kRedBlocks), dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(r), static_cast<const uint16_t*>(r_prev),
+                     n, part);
+  if (hipGetLastError() != hipSuccess) return DTA_ELAUNCH;
+  hipLaunchKernelGGL(fbcache_finish_kernel, dim3(1), dim3(256), 0, stream, part, threshold,
+                     diff, use_cache);
+  if (hipGetLastError() != hipSuccess) return DTA_ELAUNCH;
+  const int64_t want = ((n_hidden >> 3) + 255) / 256;
+  const unsigned grid = (unsigned)(want < 1 ? 1 : (want < 8192 ? want : 8192));
+  hipLaunchKernelGGL(fbcache_apply_kernel, dim3(grid), dim3(256), 0, stream,
+                     static_cast<uint16_t*>(hidden), static_cast<const uint16_t*>(cached),
+                     n_hidden, use_cache);
   return hipGetLastError() == hipSuccess ? DTA_OK : DTA_ELAUNCH;
 }
 

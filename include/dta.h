@@ -136,7 +136,8 @@ int attn_merge_into(void* o, float* lse, const void* o_part,
  * over all n elements; a is the current step's first-block residual, b the
  * previous step's. Per-thread float32 partial sums, a fixed-order float64
  * finish, so the result is bitwise reproducible. sum|b| = 0 gives the IEEE
- * quotient (+inf or NaN). The threshold compare stays with the caller.
+ * quotient (+inf or NaN). The threshold compare is the caller's, or
+ * fbcache_step's, which fuses it with the cached-residual apply.
  * Enqueues two kernels (partials, then a one-workgroup finish).
  *
  * a, b  bf16 [n], 16-byte aligned; n >= 1
@@ -146,6 +147,33 @@ int attn_merge_into(void* o, float* lse, const void* o_part,
  */
 int residual_diff(const void* a, const void* b, int64_t n, float* out,
                   void* ws, hipStream_t stream);
+
+/*
+ * fbcache_step -- First Block Cache's decision and cached-residual apply on
+ * the device, with no host round trip (ParaAttention guide, section "First
+ * Block Cache": when the first block's relative residual difference is small
+ * enough the step skips the remaining blocks and reuses their cached
+ * residual; 0.08 is FLUX's default threshold):
+ *     diff = sum|r - r_prev| / sum|r_prev|           (exactly residual_diff)
+ *     use  = diff < threshold                          (float32 compare; a NaN
+ *                                                      diff never reuses)
+ *     if use:  hidden[i] = bf16(hidden[i] + cached[i])  (float32 sum, rounded
+ *                                                      once, to nearest even)
+ * `use` is written to *use_cache (0 or 1) for later device-side work; hidden
+ * is untouched when it is 0. Enqueues three kernels: residual partials, the
+ * finish with the decision, and the apply (whose workgroups leave at once
+ * when use = 0).
+ *
+ * r, r_prev   bf16 [n], 16-byte aligned; n >= 1 (this and the previous
+ *             step's first-block residual)
+ * hidden      bf16 [n_hidden], 16-byte aligned, read and written
+ * cached      bf16 [n_hidden], 16-byte aligned (must not alias hidden)
+ * diff        float, device scalar, written;  use_cache  int, device, written
+ * ws          as for residual_diff (not concurrently with another user)
+ */
+int fbcache_step(const void* r, const void* r_prev, int64_t n, float threshold,
+                 void* hidden, const void* cached, int64_t n_hidden,
+                 float* diff, int* use_cache, void* ws, hipStream_t stream);
 
 /*
  * fp8_quant_per_tensor -- per-tensor dynamic quantisation to E4M3FN

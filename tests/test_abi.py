@@ -91,6 +91,19 @@ def test_attn_merge_into_validation():
     assert f(GOOD, GOOD, ODD, GOOD, 1, 1, 1, 128, None) == _lib.DTA_EALIGN
 
 
+def test_fbcache_step_validation():
+    f = _lib.lib().fbcache_step
+    ok = (GOOD, GOOD, 100, 0.08, GOOD, GOOD, 100, GOOD, GOOD, GOOD, None)
+    assert f(None, *ok[1:]) == _lib.DTA_EINVAL
+    assert f(GOOD, GOOD, 0, 0.08, GOOD, GOOD, 100, GOOD, GOOD, GOOD, None) == _lib.DTA_EINVAL
+    assert f(GOOD, GOOD, 100, 0.08, GOOD, GOOD, 0, GOOD, GOOD, GOOD, None) == _lib.DTA_EINVAL
+    assert f(GOOD, GOOD, 100, 0.08, GOOD, GOOD, 100, GOOD, None, GOOD, None) == _lib.DTA_EINVAL
+    assert f(GOOD, GOOD, 100, 0.08, GOOD, GOOD, 100, GOOD, GOOD, None, None) == _lib.DTA_EINVAL
+    assert f(GOOD, GOOD, 100, 0.08, ODD, GOOD, 100, GOOD, GOOD, GOOD, None) == _lib.DTA_EALIGN
+    assert f(GOOD, GOOD, 100, 0.08, GOOD, GOOD, 100, GOOD, ctypes.c_void_p(0x10002), GOOD,
+             None) == _lib.DTA_EALIGN
+
+
 def test_reductions_validation():
     lib = _lib.lib()
     assert lib.residual_diff(GOOD, GOOD, 0, GOOD, GOOD, None) == _lib.DTA_EINVAL
