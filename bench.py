@@ -316,6 +316,34 @@ def main():
         legs["fbcache_step"] = fb
         del hid, cac
 
+    # Layout kernels of context parallelism at the FLUX tensor size (P = 8):
+    # Ulysses' head split of Q for the all-to-all, and the token concat of 8
+    # received parts. Each moves 28.3 MB in and 28.3 MB out.
+    if "attn" in legs_on:
+        lay = {}
+        heads8 = [H // 8] * 8
+        toks8 = [N // 8] * 8
+        buf_h = torch.empty(q.numel(), dtype=torch.bfloat16, device=dev)
+        out_s = torch.empty_like(q)
+        for name, fn in (("head_split_P8", lambda: dta.head_split(q, heads8, parts=buf_h)),
+                         ("seq_concat_P8", lambda: dta.seq_concat(buf_h, toks8, B, H, D, out=out_s))):
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(args.steps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) / args.steps * 1e3
+            nbytes = 2 * q.numel() * 2
+            lay[name] = {"us": us, "bytes": nbytes, "GB/s": nbytes / (us * 1e-6) / 1e9,
+                         "frac_hbm_peak": nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS}
+        lay["in_step"] = False
+        legs["layout"] = lay
+        del buf_h, out_s
+
     # The same ring with the merge fused into each step (attn_fwd_accum): the
     # first chunk by attn_fwd, the other seven folded into one running (o, lse).
     # Timed apart from the step, which keeps the separate partials + merge.

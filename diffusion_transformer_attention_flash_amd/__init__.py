@@ -19,7 +19,7 @@ from . import _lib
 from ._lib import DtaError  # noqa: F401
 
 __all__ = ["attn_fwd", "attn_merge", "attn_fwd_accum", "attn_merge_into", "residual_diff",
-           "fbcache_step",
+           "fbcache_step", "seq_concat", "seq_split", "head_concat", "head_split",
            "fp8_quant_per_tensor",
            "attn_fwd_fp8", "workspace", "DtaError"]
 
@@ -190,6 +190,82 @@ def fbcache_step(r, r_prev, threshold, hidden, cached, diff=None, use_cache=None
                                  _ptr(use_cache), _ptr(ws), ctypes_ptr(_stream(r)))
     _lib.check("fbcache_step", st)
     return diff, use_cache
+
+
+def _host_ints(vals, name):
+    import ctypes
+    vals = [int(x) for x in vals]
+    if not vals:
+        raise ValueError("%s must not be empty" % name)
+    return (ctypes.c_int * len(vals))(*vals), len(vals)
+
+
+def _layout_check(t, name, numel):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError("%s must be a CUDA tensor" % name)
+    if t.element_size() != 2 or not t.is_contiguous():
+        raise ValueError("%s must be a contiguous 16-bit tensor" % name)
+    if t.numel() != numel:
+        raise ValueError("%s has %d elements, expected %d" % (name, t.numel(), numel))
+
+
+def seq_concat(parts, lens, B, H, D, padded=None, out=None):
+    """Concatenate P token-parts (packed back to back, part p = [B,H,padded[p],D]
+    with lens[p] valid tokens) into out [B,H,sum(lens),D]."""
+    pads = list(lens) if padded is None else list(padded)
+    _layout_check(parts, "parts", B * H * sum(pads) * D)
+    if out is None:
+        out = torch.empty((B, H, sum(lens), D), dtype=parts.dtype, device=parts.device)
+    _layout_check(out, "out", B * H * sum(lens) * D)
+    cl, n = _host_ints(lens, "lens")
+    cp, _ = _host_ints(pads, "padded")
+    st = _lib.lib().seq_concat(_ptr(parts), _ptr(out), n, cl, cp, B, H, D,
+                               ctypes_ptr(_stream(parts)))
+    _lib.check("seq_concat", st)
+    return out
+
+
+def seq_split(x, lens, padded=None, parts=None):
+    """Split x [B,H,sum(lens),D] along tokens into packed parts [B,H,padded[p],D]
+    (padding rows zero); returns the flat packed buffer."""
+    B, H, S, D = x.shape
+    pads = list(lens) if padded is None else list(padded)
+    _layout_check(x, "x", B * H * sum(lens) * D)
+    if parts is None:
+        parts = torch.empty(B * H * sum(pads) * D, dtype=x.dtype, device=x.device)
+    _layout_check(parts, "parts", B * H * sum(pads) * D)
+    cl, n = _host_ints(lens, "lens")
+    cp, _ = _host_ints(pads, "padded")
+    st = _lib.lib().seq_split(_ptr(x), _ptr(parts), n, cl, cp, B, H, D, ctypes_ptr(_stream(x)))
+    _lib.check("seq_split", st)
+    return parts
+
+
+def head_concat(parts, heads, B, N, D, out=None):
+    """Concatenate P head-parts (packed, part p = [B,heads[p],N,D]) into
+    out [B,sum(heads),N,D]."""
+    _layout_check(parts, "parts", B * sum(heads) * N * D)
+    if out is None:
+        out = torch.empty((B, sum(heads), N, D), dtype=parts.dtype, device=parts.device)
+    _layout_check(out, "out", B * sum(heads) * N * D)
+    ch, n = _host_ints(heads, "heads")
+    st = _lib.lib().head_concat(_ptr(parts), _ptr(out), n, ch, B, N, D, ctypes_ptr(_stream(parts)))
+    _lib.check("head_concat", st)
+    return out
+
+
+def head_split(x, heads, parts=None):
+    """Split x [B,sum(heads),N,D] along heads into packed parts [B,heads[p],N,D];
+    returns the flat packed buffer."""
+    B, Hs, N, D = x.shape
+    _layout_check(x, "x", B * sum(heads) * N * D)
+    if parts is None:
+        parts = torch.empty(x.numel(), dtype=x.dtype, device=x.device)
+    _layout_check(parts, "parts", x.numel())
+    ch, n = _host_ints(heads, "heads")
+    st = _lib.lib().head_split(_ptr(x), _ptr(parts), n, ch, B, N, D, ctypes_ptr(_stream(x)))
+    _lib.check("head_split", st)
+    return parts
 
 
 def fp8_quant_per_tensor(x, x8=None, descale=None):

@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libdta.so")
 
-SOURCES = ["attn_fwd.hip", "attn_fwd_fp8.hip", "merge.hip", "reduce.hip"]
+SOURCES = ["attn_fwd.hip", "attn_fwd_fp8.hip", "merge.hip", "reduce.hip", "layout.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -210,6 +210,42 @@ int attn_fwd_fp8(const void* q8, const void* k8, const void* v8,
                  const float* descale, void* o, float* lse, int B, int H,
                  int Nq, int Nkv, int D, float scale, hipStream_t stream);
 
+/*
+ * Layout kernels of context parallelism (diffusers "Context parallelism"
+ * guide): the local permutations on either side of the exchanges.
+ * - Ulysses Attention: an all-to-all turns [B,H,n_rank,D] (all heads, this
+ *   rank's tokens) into [B,H_rank,N,D] (this rank's heads, all tokens) and
+ *   back. The sender splits along one axis into per-destination parts, the
+ *   receiver concatenates the received parts along the other. Ulysses
+ *   Anything Attention allows uneven parts on both axes.
+ * - Ring Anything Attention: ranks hold uneven token counts; each part is
+ *   padded to the longest for the all-gather and the padding is dropped when
+ *   the gathered parts are concatenated.
+ * Parts are stored back to back in one buffer, part p first. Sizes are HOST
+ * arrays of P ints (1 <= P <= 64). Any D that is a multiple of 8 works
+ * (rows move as 16-byte chunks); every element is bf16 / 2 bytes, so the
+ * kernels copy any 16-bit payload exactly. Buffers must not overlap.
+ *
+ * seq_concat  parts: part p = [B,H,padded[p],D] whose first lens[p] tokens
+ *             are valid; out = [B,H,sum lens,D], part p's tokens at offset
+ *             lens[0]+...+lens[p-1]. padded NULL means padded = lens.
+ *             lens[p] >= 0, padded[p] >= max(lens[p], 1), sum lens >= 1.
+ * seq_split   the inverse: x = [B,H,sum lens,D] -> parts; tokens lens[p] ..
+ *             padded[p]-1 of each part are written as zeros.
+ * head_concat parts: part p = [B,heads[p],N,D]; out = [B,sum heads,N,D].
+ * head_split  the inverse. heads[p] >= 1.
+ * All are 16-byte aligned device buffers. Return DTA_OK, DTA_EINVAL (bad
+ * sizes, P out of range, D not a multiple of 8), DTA_EALIGN or DTA_ELAUNCH.
+ */
+int seq_concat(const void* parts, void* out, int P, const int* lens,
+               const int* padded, int B, int H, int D, hipStream_t stream);
+int seq_split(const void* x, void* parts, int P, const int* lens,
+              const int* padded, int B, int H, int D, hipStream_t stream);
+int head_concat(const void* parts, void* out, int P, const int* heads, int B,
+                int N, int D, hipStream_t stream);
+int head_split(const void* x, void* parts, int P, const int* heads, int B,
+               int N, int D, hipStream_t stream);
+
 /* Bytes of the workspace residual_diff and fp8_quant_per_tensor need. */
 size_t dta_ws_bytes(void);
 

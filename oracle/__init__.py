@@ -24,6 +24,10 @@ What it computes, each written from the plain definition (numpy, float64):
 * ``fbcache_step``    -- First Block Cache's decision (float32(diff) <
                          threshold) and cached-residual apply, hidden +=
                          cached rounded once to bfloat16 (same section).
+* ``layout``          -- seq/head split and concat with uneven and padded
+                         parts, the permutations around Ulysses and Ring
+                         Anything exchanges (diffusers "Context parallelism"
+                         guide).
 * ``e4m3_encode`` / ``e4m3_decode`` / ``quant_per_tensor`` /
   ``attention_fp8``   -- per-tensor dynamic fp8 (OCP E4M3FN) quantisation
                          and attention on the dequantised values with the
@@ -37,10 +41,11 @@ closed forms, invariants, a library float8 cast). None is "parity unpinned".
 
 from .attention import attention, merge, softmax_rows
 from .residual import fbcache_step, residual_diff
+from . import layout
 from .fp8 import (E4M3_MAX, e4m3_decode, e4m3_encode, quant_per_tensor,
                   attention_fp8)
 
 __all__ = [
-    "attention", "merge", "softmax_rows", "residual_diff", "fbcache_step", "E4M3_MAX",
+    "attention", "merge", "softmax_rows", "residual_diff", "fbcache_step", "layout", "E4M3_MAX",
     "e4m3_decode", "e4m3_encode", "quant_per_tensor", "attention_fp8",
 ]

@@ -104,6 +104,25 @@ def test_fbcache_step_validation():
              None) == _lib.DTA_EALIGN
 
 
+def test_layout_validation():
+    lib = _lib.lib()
+    I = ctypes.c_int
+    two = (I * 2)(3, 4)
+    pads = (I * 2)(3, 5)
+    bad_pads = (I * 2)(2, 5)                      # padded < lens
+    zeros = (I * 2)(0, 0)
+    assert lib.seq_concat(GOOD, GOOD, 0, two, pads, 1, 2, 128, None) == _lib.DTA_EINVAL
+    assert lib.seq_concat(GOOD, GOOD, 65, two, pads, 1, 2, 128, None) == _lib.DTA_EINVAL
+    assert lib.seq_concat(GOOD, GOOD, 2, None, pads, 1, 2, 128, None) == _lib.DTA_EINVAL
+    assert lib.seq_concat(GOOD, GOOD, 2, two, bad_pads, 1, 2, 128, None) == _lib.DTA_EINVAL
+    assert lib.seq_concat(GOOD, GOOD, 2, zeros, pads, 1, 2, 128, None) == _lib.DTA_EINVAL
+    assert lib.seq_split(GOOD, GOOD, 2, two, None, 1, 2, 100, None) == _lib.DTA_EINVAL  # D % 8
+    assert lib.seq_split(GOOD, ODD, 2, two, None, 1, 2, 128, None) == _lib.DTA_EALIGN
+    assert lib.head_concat(GOOD, GOOD, 2, zeros, 1, 8, 128, None) == _lib.DTA_EINVAL  # heads >= 1
+    assert lib.head_split(None, GOOD, 2, two, 1, 8, 128, None) == _lib.DTA_EINVAL
+    assert lib.head_split(ODD, GOOD, 2, two, 1, 8, 128, None) == _lib.DTA_EALIGN
+
+
 def test_reductions_validation():
     lib = _lib.lib()
     assert lib.residual_diff(GOOD, GOOD, 0, GOOD, GOOD, None) == _lib.DTA_EINVAL

@@ -483,3 +483,84 @@ def test_fbcache_decision_is_taken_in_float32():
     assert d == 1.0 / 3.0 and use is False        # equal in float32: not below
     d, use, _ = oracle.fbcache_step(a, b, float(np.nextafter(np.float32(1.0 / 3.0), np.float32(1))), h, h)
     assert use is True
+
+
+# ---- layout permutations (context-parallel split / concat) ----------------
+
+def _arange(shape):
+    return np.arange(int(np.prod(shape)), dtype=np.int64).reshape(shape)
+
+
+def test_layout_seq_split_positions_by_formula():
+    B, H, D = 2, 3, 4
+    lens, pads = [3, 0, 5, 1], [4, 2, 5, 3]
+    S = sum(lens)
+    x = _arange((B, H, S, D))
+    parts = oracle.layout.seq_split(x, lens, pads)
+    off = 0
+    for p, (n, pad) in enumerate(zip(lens, pads)):
+        assert parts[p].shape == (B, H, pad, D)
+        for b in range(B):
+            for h in range(H):
+                for t in range(pad):
+                    for d in range(D):
+                        want = ((b * H + h) * S + off + t) * D + d if t < n else 0
+                        assert parts[p][b, h, t, d] == want
+        off += n
+    assert np.array_equal(oracle.layout.seq_concat(parts, lens), x)
+
+
+def test_layout_head_split_positions_by_formula():
+    B, N, D = 2, 5, 3
+    heads = [1, 3, 2]
+    Hs = sum(heads)
+    x = _arange((B, Hs, N, D))
+    parts = oracle.layout.head_split(x, heads)
+    hoff = 0
+    for p, hp in enumerate(heads):
+        assert parts[p].shape == (B, hp, N, D)
+        for b in range(B):
+            for hl in range(hp):
+                for n in range(N):
+                    for d in range(D):
+                        assert parts[p][b, hl, n, d] == ((b * Hs + hoff + hl) * N + n) * D + d
+        hoff += hp
+    assert np.array_equal(oracle.layout.head_concat(parts), x)
+
+
+def test_layout_ulysses_round_trip_matches_global_slicing():
+    """P ranks, uneven tokens and heads: head_split on every rank, the
+    all-to-all as a transpose of the part lists, seq_concat on every rank must
+    give each rank all tokens of its heads; the reverse path must give the
+    ranks back their token shards."""
+    B, D = 1, 8
+    n_rank = [5, 3, 7]
+    h_rank = [2, 1, 3]
+    N, H = sum(n_rank), sum(h_rank)
+    g = np.random.default_rng(3)
+    X = g.standard_normal((B, H, N, D))
+    toff = np.concatenate([[0], np.cumsum(n_rank)])
+    hoff = np.concatenate([[0], np.cumsum(h_rank)])
+    local = [X[:, :, toff[r]:toff[r + 1]] for r in range(3)]
+    sent = [oracle.layout.head_split(local[r], h_rank) for r in range(3)]
+    recv = [[sent[s][r] for s in range(3)] for r in range(3)]          # all-to-all
+    gathered = [oracle.layout.seq_concat(recv[r], n_rank) for r in range(3)]
+    for r in range(3):
+        assert np.array_equal(gathered[r], X[:, hoff[r]:hoff[r + 1]])
+    back_sent = [oracle.layout.seq_split(gathered[r], n_rank) for r in range(3)]
+    back_recv = [[back_sent[s][r] for s in range(3)] for r in range(3)]
+    for r in range(3):
+        assert np.array_equal(oracle.layout.head_concat(back_recv[r]), local[r])
+
+
+def test_layout_ring_anything_pad_gather_trim():
+    """Uneven token shards padded to the longest, all-gathered, trimmed."""
+    B, H, D = 1, 2, 8
+    n_rank = [4, 1, 6]
+    m = max(n_rank)
+    g = np.random.default_rng(4)
+    shards = [g.standard_normal((B, H, n, D)) for n in n_rank]
+    padded = [oracle.layout.seq_split(s, [s.shape[2]], [m])[0] for s in shards]
+    assert all(p.shape[2] == m for p in padded)
+    full = oracle.layout.seq_concat(padded, n_rank)
+    assert np.array_equal(full, np.concatenate(shards, axis=2))
