@@ -33,6 +33,9 @@ What it computes, each written from the plain definition (numpy, float64):
                          and attention on the dequantised values with the
                          probabilities quantised before the P.V product
                          (ParaAttention guide, section "fp8 quantization").
+* ``quant_rows_pow2`` / ``attention_fp8_rows`` -- the row-wise variant the
+                         same section names as more accurate: one
+                         power-of-two scale per token for Q and K.
 
 Every function is pinned by tests in ``tests/test_oracle_pins.py`` against
 mathematics it does not share code with (arbitrary-precision brute force,
@@ -42,10 +45,12 @@ closed forms, invariants, a library float8 cast). None is "parity unpinned".
 from .attention import attention, merge, softmax_rows
 from .residual import fbcache_step, residual_diff
 from . import layout
-from .fp8 import (E4M3_MAX, e4m3_decode, e4m3_encode, quant_per_tensor,
+from .fp8 import (E4M3_MAX, e4m3_decode, e4m3_encode, quant_per_tensor, quant_rows_pow2,
+                  attention_fp8_rows,
                   attention_fp8)
 
 __all__ = [
     "attention", "merge", "softmax_rows", "residual_diff", "fbcache_step", "layout", "E4M3_MAX",
     "e4m3_decode", "e4m3_encode", "quant_per_tensor", "attention_fp8",
+    "quant_rows_pow2", "attention_fp8_rows",
 ]

@@ -97,6 +97,53 @@ def attention_fp8(q8, k8, v8, descale, scale, rows=None):
     q = e4m3_decode(np.asarray(q8)) * float(descale[0])
     k = e4m3_decode(np.asarray(k8)) * float(descale[1])
     v = e4m3_decode(np.asarray(v8)) * float(descale[2])
+    return _attention_p8(q, k, v, scale, rows)
+
+
+def quant_rows_pow2(x, row_len):
+    """Row-wise dynamic quantisation to E4M3FN with power-of-two scales.
+
+    ParaAttention guide, section "fp8 quantization": per-tensor scaling is
+    the default and row-wise scaling the more accurate option. Each row of
+    ``row_len`` consecutive elements (one token of one head for Q and K) gets
+    its own scale 2^e with e the smallest integer such that amax_row <=
+    448 * 2^e, clamped to [-127, 127] (e = 0 for an all-zero row); codes are
+    e4m3(x * 2^-e), the scaling exact. A power of two loses nothing against
+    amax/448: E4M3 keeps 3 mantissa bits in every binade, so only the
+    saturation and underflow limits depend on the scale, and these are set
+    the same way. Returns (codes uint8 of x's shape, exponents as E8M0 bytes
+    e + 127, one per row).
+    """
+    if hasattr(x, "detach"):
+        import torch
+        x = x.detach().to("cpu").to(torch.float32).numpy()
+    x64 = np.asarray(x, dtype=np.float32).astype(np.float64)
+    if row_len < 1 or x64.size % row_len:
+        raise ValueError("row_len must divide the element count")
+    rows = x64.reshape(-1, row_len)
+    amax = np.abs(rows).max(axis=1)
+    m, k = np.frexp(amax)                     # amax = m * 2^k, 0.5 <= m < 1
+    # 448 = 0.875 * 2^9: amax <= 448 * 2^e  <=>  e >= k - 9 (m <= 0.875) or k - 8
+    e = np.where(m <= 0.875, k - 9, k - 8)
+    e = np.where(amax == 0, 0, np.clip(e, -127, 127)).astype(np.int64)
+    codes = e4m3_encode(rows * np.ldexp(1.0, -e)[:, None])
+    return codes.reshape(np.shape(x)), (e + 127).astype(np.uint8)
+
+
+def attention_fp8_rows(q8, k8, v8, q_e8m0, k_e8m0, s_v, scale, rows=None):
+    """Attention on row-scaled E4M3 Q and K (one power-of-two scale per token,
+    E8M0 bytes [B,H,N]) and per-tensor E4M3 V (scale s_v), with P quantised
+    to E4M3 at x448 exactly as ``attention_fp8``."""
+    q = e4m3_decode(np.asarray(q8)) * np.ldexp(1.0, np.asarray(q_e8m0, dtype=np.int64) - 127)[..., None]
+    k = e4m3_decode(np.asarray(k8)) * np.ldexp(1.0, np.asarray(k_e8m0, dtype=np.int64) - 127)[..., None]
+    v = e4m3_decode(np.asarray(v8)) * float(s_v)
+    return _attention_p8(q, k, v, scale, rows)
+
+
+def _attention_p8(q, k, v, scale, rows):
+    """Softmax attention on dequantised float64 q, k, v with the
+    probabilities rounded to E4M3 at x448 before the P.V product and the
+    normaliser taken from the unrounded probabilities."""
     B, H, Nq, D = q.shape
     if k.shape[2] < 1:
         raise ValueError("Nkv must be >= 1")

@@ -564,3 +564,62 @@ def test_layout_ring_anything_pad_gather_trim():
     assert all(p.shape[2] == m for p in padded)
     full = oracle.layout.seq_concat(padded, n_rank)
     assert np.array_equal(full, np.concatenate(shards, axis=2))
+
+
+# ---- row-wise power-of-two fp8 scales (quant_rows_pow2, attention_fp8_rows) ----
+
+def test_rows_pow2_exponent_is_minimal():
+    vals = []
+    for k in (-20, -3, 0, 1, 9, 30):
+        base = 448.0 * 2.0 ** k
+        vals += [base, base * (1 + 2.0 ** -7), base * (1 - 2.0 ** -8), base / 3.0]
+    vals += [1e-38, 1e-36, 3.0e38]
+    x = torch.tensor(vals, dtype=torch.float32).to(torch.bfloat16).reshape(-1, 1)
+    x = torch.cat([x, -x / 2], dim=1)                      # rows of 2, amax = |first|
+    codes, e8 = oracle.quant_rows_pow2(x, 2)
+    amax = x.float().abs().amax(dim=1).double().numpy()
+    e = e8.astype(np.int64) - 127
+    for a, ee in zip(amax, e):
+        assert a <= 448.0 * 2.0 ** ee
+        assert ee == -127 or a > 448.0 * 2.0 ** (ee - 1)
+    z = torch.zeros(3, 4, dtype=torch.bfloat16)
+    c0, e0 = oracle.quant_rows_pow2(z, 4)
+    assert (e0 == 127).all() and (c0 == 0).all()
+
+
+def test_rows_pow2_codes_match_torch_and_error_bound():
+    g = torch.Generator().manual_seed(21)
+    x = (torch.randn(64, 128, generator=g) *
+         torch.exp2(torch.randint(-8, 8, (64, 1), generator=g).float())).to(torch.bfloat16)
+    codes, e8 = oracle.quant_rows_pow2(x, 128)
+    scale = torch.exp2(torch.from_numpy(e8.astype(np.float32)) - 127)[:, None]
+    ref = (x.float() / scale).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(codes, ref)
+    back = oracle.e4m3_decode(codes) * scale.double().numpy()
+    xs = x.double().numpy()
+    big = np.abs(xs) >= 2.0 ** -6 * scale.double().numpy()       # E4M3 normal range
+    assert (np.abs(back - xs)[big] <= 2.0 ** -4 * np.abs(xs)[big]).all()
+    assert np.abs(oracle.e4m3_decode(codes)).max() <= 448.0
+
+
+def test_rows_pow2_attention_beats_per_tensor_on_outlier_tokens():
+    """One outlier token per head (x 2^16) crushes every other row of a
+    per-tensor quantised Q into E4M3's subnormals; per-row scales do not."""
+    B, H, N, D = 1, 2, 96, 64
+    q, k, v = workloads.make_qkv(9, B, H, N, N, D)
+    q = q.float()
+    q[:, :, 5] *= 65536.0
+    q = q.to(torch.bfloat16)
+    scale = D ** -0.5
+    o_ref, _ = oracle.attention(q, k, v, scale)
+    qt, sq = oracle.quant_per_tensor(q)
+    kt, sk = oracle.quant_per_tensor(k)
+    vt, sv = oracle.quant_per_tensor(v)
+    o_t, _ = oracle.attention_fp8(qt, kt, vt, (sq, sk, sv), scale)
+    qr, eq = oracle.quant_rows_pow2(q, D)
+    kr, ek = oracle.quant_rows_pow2(k, D)
+    o_r, _ = oracle.attention_fp8_rows(qr, kr, vt, eq.reshape(B, H, N), ek.reshape(B, H, N), sv, scale)
+    rows = [i for i in range(N) if i != 5]
+    err_t = np.linalg.norm((o_t - o_ref)[:, :, rows]) / np.linalg.norm(o_ref[:, :, rows])
+    err_r = np.linalg.norm((o_r - o_ref)[:, :, rows]) / np.linalg.norm(o_ref[:, :, rows])
+    assert err_r < 0.08 and err_t > 3 * err_r, (err_r, err_t)
