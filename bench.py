@@ -316,6 +316,41 @@ def main():
         legs["fbcache_step"] = fb
         del hid, cac
 
+    # Row-wise fp8 (per-token power-of-two Q/K scales applied by the MFMA
+    # operand scales, per-tensor V) at the FLUX shape, outside the step.
+    if "fp8" in legs_on:
+        rq8 = torch.empty_like(q8)
+        rk8 = torch.empty_like(q8)
+        req = torch.empty((B, H, N), dtype=torch.uint8, device=dev)
+        rek = torch.empty_like(req)
+        ro = torch.empty_like(q)
+        rl = torch.empty_like(lse)
+        rows_legs = {}
+        for name, fn in (
+                ("quant_rows_q_and_k", lambda: (dta.fp8_quant_rows_pow2(q, x8=rq8, e8m0=req),
+                                                dta.fp8_quant_rows_pow2(k, x8=rk8, e8m0=rek))),
+                ("attn_fwd_fp8_rows", lambda: dta.attn_fwd_fp8_rows(rq8, rk8, v8, req, rek, ds[2:3],
+                                                                    scale, o=ro, lse=rl))):
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(args.steps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / args.steps
+            rows_legs[name] = {"ms": ms}
+        qb = 2 * (q.numel() * 2 + q.numel() + B * H * N)
+        rows_legs["quant_rows_q_and_k"]["GB/s"] = qb / (rows_legs["quant_rows_q_and_k"]["ms"] * 1e-3) / 1e9
+        tf = flop_full / (rows_legs["attn_fwd_fp8_rows"]["ms"] * 1e-3) / 1e12
+        rows_legs["attn_fwd_fp8_rows"]["TFLOP/s"] = tf
+        rows_legs["attn_fwd_fp8_rows"]["frac_fp8_peak"] = tf / PEAK_FP8_TFLOPS
+        rows_legs["in_step"] = False
+        legs["fp8_rows"] = rows_legs
+        del rq8, rk8, req, rek, ro, rl
+
     # Layout kernels of context parallelism at the FLUX tensor size (P = 8):
     # Ulysses' head split of Q for the all-to-all, and the token concat of 8
     # received parts. Each moves 28.3 MB in and 28.3 MB out.

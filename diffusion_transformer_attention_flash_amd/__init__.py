@@ -20,6 +20,7 @@ from ._lib import DtaError  # noqa: F401
 
 __all__ = ["attn_fwd", "attn_merge", "attn_fwd_accum", "attn_merge_into", "residual_diff",
            "fbcache_step", "seq_concat", "seq_split", "head_concat", "head_split",
+           "fp8_quant_rows_pow2", "attn_fwd_fp8_rows",
            "fp8_quant_per_tensor",
            "attn_fwd_fp8", "workspace", "DtaError"]
 
@@ -310,4 +311,57 @@ def attn_fwd_fp8(q8, k8, v8, descale, scale=None, o=None, lse=None):
                                  _ptr(lse), B, H, Nq, Nkv, D, float(scale),
                                  ctypes_ptr(_stream(q8)))
     _lib.check("attn_fwd_fp8", st)
+    return o, lse
+
+
+def fp8_quant_rows_pow2(x, row_len=None, x8=None, e8m0=None):
+    """Row-wise E4M3 quantisation with power-of-two scales. Rows are the
+    last dimension of x unless row_len is given. Returns (x8 uint8 with x's
+    shape, e8m0 uint8 [rows]); the scale of row r is 2^(e8m0[r] - 127)."""
+    _need(x, "x", torch.bfloat16)
+    if row_len is None:
+        row_len = x.shape[-1]
+    if x.numel() % row_len:
+        raise ValueError("row_len must divide the element count")
+    rows = x.numel() // row_len
+    if x8 is None:
+        x8 = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    if e8m0 is None:
+        e8m0 = torch.empty(x.shape[:-1] if row_len == x.shape[-1] else (rows,),
+                           dtype=torch.uint8, device=x.device)
+    _need(x8, "x8", torch.uint8)
+    _need(e8m0, "e8m0", torch.uint8)
+    if x8.numel() != x.numel() or e8m0.numel() != rows:
+        raise ValueError("x8 / e8m0 sizes do not match")
+    st = _lib.lib().fp8_quant_rows_pow2(_ptr(x), rows, int(row_len), _ptr(x8), _ptr(e8m0),
+                                        ctypes_ptr(_stream(x)))
+    _lib.check("fp8_quant_rows_pow2", st)
+    return x8, e8m0
+
+
+def attn_fwd_fp8_rows(q8, k8, v8, q_e8m0, k_e8m0, v_descale, scale=None, o=None, lse=None):
+    """fp8 attention with per-token power-of-two Q/K scales (E8M0 bytes
+    [B,H,N]) and V's per-tensor scale (f32[1])."""
+    _need(q8, "q8", torch.uint8, 4)
+    _need(k8, "k8", torch.uint8, 4)
+    _need(v8, "v8", torch.uint8, 4)
+    _need(q_e8m0, "q_e8m0", torch.uint8)
+    _need(k_e8m0, "k_e8m0", torch.uint8)
+    _need(v_descale, "v_descale", torch.float32)
+    B, H, Nq, D = q8.shape
+    Nkv = k8.shape[2]
+    if tuple(k8.shape) != (B, H, Nkv, D) or tuple(v8.shape) != (B, H, Nkv, D):
+        raise ValueError("shape mismatch")
+    if q_e8m0.numel() != B * H * Nq or k_e8m0.numel() != B * H * Nkv:
+        raise ValueError("q_e8m0 / k_e8m0 must hold one byte per token of each head")
+    if scale is None:
+        scale = D ** -0.5
+    if o is None:
+        o = torch.empty((B, H, Nq, D), dtype=torch.bfloat16, device=q8.device)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q8.device)
+    st = _lib.lib().attn_fwd_fp8_rows(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(q_e8m0), _ptr(k_e8m0),
+                                      _ptr(v_descale), _ptr(o), _ptr(lse), B, H, Nq, Nkv, D,
+                                      float(scale), ctypes_ptr(_stream(q8)))
+    _lib.check("attn_fwd_fp8_rows", st)
     return o, lse

@@ -77,10 +77,14 @@ __device__ __forceinline__ i32x8 cat8(u32x4 lo, u32x4 hi) {
                (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
 }
 
-template <int D, int NW>
+// ROWS: Q and K carry one power-of-two scale per token (E8M0 bytes q_e8,
+// k_e8); the score MFMA applies them through its operand scales (A row =
+// key, B column = query), and descale[0] is V's per-tensor scale.
+template <int D, int NW, bool ROWS>
 __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_fp8_kernel(
     const uint8_t* __restrict__ q, const uint8_t* __restrict__ k,
     const uint8_t* __restrict__ v, const float* __restrict__ descale,
+    const uint8_t* __restrict__ q_e8, const uint8_t* __restrict__ k_e8,
     uint16_t* __restrict__ o, float* __restrict__ lse, int Nq, int Nkv,
     float scale, int n_qt) {
   using C = Fp8Cfg<D, NW>;
@@ -98,8 +102,13 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_fp8_kernel(
   const uint8_t* vh = v + (int64_t)bh * Nkv * D;
   const int row = qt * C::kBM + wave * 32 + l32;
 
-  const float s_q = descale[0], s_k = descale[1], s_v = descale[2];
+  const float s_q = ROWS ? 1.0f : descale[0], s_k = ROWS ? 1.0f : descale[1];
+  const float s_v = ROWS ? descale[0] : descale[2];
   const float c = scale * s_q * s_k * kLog2e;
+  // E8M0 operand scales of the score MFMA (127 = 2^0).
+  const int sq_e = (ROWS && row < Nq) ? (int)q_e8[(int64_t)bh * Nq + row] : 127;
+  const uint8_t* ke_h = ROWS ? k_e8 + (int64_t)bh * Nkv : nullptr;
+  int sk_next[2] = {127, 127};
 
   // Q^T operand: 32 bytes (dims kk*64 + 32g .. +31) per 64-dim step.
   i32x8 qr[D / 64];
@@ -131,6 +140,16 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_fp8_kernel(
       kreg[it] = __builtin_amdgcn_raw_buffer_load_b128(kr, off, 0, 0);
       vreg[it] = __builtin_amdgcn_raw_buffer_load_b128(vr, off, 0, 0);
     }
+    if constexpr (ROWS) {
+      // Scales of the keys this lane's A rows hold, through a byte-ranged
+      // buffer resource: keys past Nkv read 0 (2^-127) without a branch;
+      // their K rows are zero and their scores are masked anyway.
+      const __amdgpu_buffer_rsrc_t er = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(ke_h + key0), 0, (int)min<int64_t>(Nkv - key0, BN), kBufDword3Fp8);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        sk_next[kb] = (int)__builtin_amdgcn_raw_buffer_load_b8(er, kb * 32 + l32, 0, 0);
+    }
   };
   auto store_tile = [&](int buf) {
 #pragma unroll
@@ -161,6 +180,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_fp8_kernel(
     constexpr bool MASK = decltype(mask_tag)::value;
     constexpr int buf = decltype(buf_tag)::value;
     const bool has_next = j + 1 < n_tiles;
+    const int sk_e[2] = {sk_next[0], sk_next[1]};
     if (has_next) load_tile(j + 1);
     const uint8_t* kt = ks[buf];
     const uint8_t* vt = vs[buf];
@@ -171,8 +191,12 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_fp8_kernel(
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const u32x4* src = reinterpret_cast<const u32x4*>(kt + k_base + kb * 32 * C::kKS + kk * 64);
-        s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            cat8(src[0], src[1]), qr[kk], s[kb], 0, 0, 0, 0, 0, 0);
+        if constexpr (ROWS)
+          s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              cat8(src[0], src[1]), qr[kk], s[kb], 0, 0, 0, sk_e[kb], 0, sq_e);
+        else
+          s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              cat8(src[0], src[1]), qr[kk], s[kb], 0, 0, 0, 0, 0, 0);
       }
 
     const int key_lim = Nkv - j * BN;
@@ -273,18 +297,20 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_fp8_kernel(
   }
 }
 
-template <int D, int NW>
+template <int D, int NW, bool ROWS>
 static int launch_fp8(const void* q8, const void* k8, const void* v8,
-                      const float* descale, void* o, float* lse, int B, int H,
-                      int Nq, int Nkv, float scale, hipStream_t stream) {
+                      const float* descale, const void* q_e8, const void* k_e8, void* o,
+                      float* lse, int B, int H, int Nq, int Nkv, float scale,
+                      hipStream_t stream) {
   using C = Fp8Cfg<D, NW>;
   const int n_qt = (Nq + C::kBM - 1) / C::kBM;
   const int64_t grid = (int64_t)n_qt * B * H;
   if (grid > 0x7FFFFFFF) return DTA_EUNSUPPORTED;
-  hipLaunchKernelGGL((attn_fwd_fp8_kernel<D, NW>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((attn_fwd_fp8_kernel<D, NW, ROWS>), dim3((unsigned)grid),
                      dim3(C::kThreads), 0, stream,
                      static_cast<const uint8_t*>(q8), static_cast<const uint8_t*>(k8),
                      static_cast<const uint8_t*>(v8), descale,
+                     static_cast<const uint8_t*>(q_e8), static_cast<const uint8_t*>(k_e8),
                      static_cast<uint16_t*>(o), lse, Nq, Nkv, scale, n_qt);
   return hipGetLastError() == hipSuccess ? DTA_OK : DTA_ELAUNCH;
 }
@@ -308,6 +334,29 @@ extern "C" int attn_fwd_fp8(const void* q8, const void* k8, const void* v8,
       (lse && !al(lse, 4)))
     return DTA_EALIGN;
   if (D == 128)
-    return launch_fp8<128, 4>(q8, k8, v8, descale, o, lse, B, H, Nq, Nkv, scale, stream);
-  return launch_fp8<64, 4>(q8, k8, v8, descale, o, lse, B, H, Nq, Nkv, scale, stream);
+    return launch_fp8<128, 4, false>(q8, k8, v8, descale, nullptr, nullptr, o, lse, B, H, Nq,
+                                     Nkv, scale, stream);
+  return launch_fp8<64, 4, false>(q8, k8, v8, descale, nullptr, nullptr, o, lse, B, H, Nq, Nkv,
+                                  scale, stream);
+}
+
+extern "C" int attn_fwd_fp8_rows(const void* q8, const void* k8, const void* v8,
+                                 const void* q_e8m0, const void* k_e8m0,
+                                 const float* v_descale, void* o, float* lse, int B, int H,
+                                 int Nq, int Nkv, int D, float scale, hipStream_t stream) {
+  if (!q8 || !k8 || !v8 || !q_e8m0 || !k_e8m0 || !v_descale || !o) return DTA_EINVAL;
+  if (B < 1 || H < 1 || Nq < 1 || Nkv < 1) return DTA_EINVAL;
+  if (!(scale >= 0.f) || !__builtin_isfinite(scale)) return DTA_EINVAL;
+  if (D != 64 && D != 128) return DTA_EUNSUPPORTED;
+  auto al = [](const void* p, uintptr_t a) {
+    return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0;
+  };
+  if (!al(q8, 16) || !al(k8, 16) || !al(v8, 16) || !al(o, 16) || !al(v_descale, 4) ||
+      (lse && !al(lse, 4)))
+    return DTA_EALIGN;
+  if (D == 128)
+    return launch_fp8<128, 4, true>(q8, k8, v8, v_descale, q_e8m0, k_e8m0, o, lse, B, H, Nq,
+                                    Nkv, scale, stream);
+  return launch_fp8<64, 4, true>(q8, k8, v8, v_descale, q_e8m0, k_e8m0, o, lse, B, H, Nq, Nkv,
+                                 scale, stream);
 }

@@ -3,6 +3,8 @@
 //   sum|a-b| / sum|b| (ParaAttention guide, section "First Block Cache").
 // * fbcache_step -- the same reduction, the cache decision diff < threshold
 //   into a device flag, and the flag-guarded apply hidden += cached.
+// * fp8_quant_rows_pow2 -- row-wise E4M3 quantisation with one power-of-two
+//   scale per row (the same section's more accurate option).
 // * fp8_quant_per_tensor -- per-tensor dynamic E4M3FN quantisation, scale
 //   amax|x|/448 (ParaAttention guide, section "fp8 quantization").
 //
@@ -249,6 +251,54 @@ __global__ __launch_bounds__(256) void fp8_cast_kernel(
   }
 }
 
+// Row-wise power-of-two E4M3 quantisation: one 16-lane group per row of
+// row_len (a multiple of 8) elements, 16-byte chunks. The exponent is the
+// smallest e with amax <= 448 * 2^e, read off the bf16 bits of amax exactly:
+// amax = (1 + f/128) 2^(E-127) is <= 448 * 2^e = 1.75 * 2^(8+e) iff
+// e >= E-135 when f <= 96 (1 + f/128 <= 1.75), else e >= E-134. Scaling by
+// 2^-e is exact (v_ldexp), then saturating RNE conversion.
+__global__ __launch_bounds__(256) void fp8_rows_pow2_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, int row_len, uint8_t* __restrict__ x8,
+    uint8_t* __restrict__ e8m0) {
+  const int grp = threadIdx.x >> 4, l16 = threadIdx.x & 15;
+  const int cpr = row_len >> 3;
+  for (int64_t r = (int64_t)blockIdx.x * 16 + grp; r < rows; r += (int64_t)gridDim.x * 16) {
+    const u32x4* xr = reinterpret_cast<const u32x4*>(x + r * row_len);
+    uint32_t m = 0;
+    for (int c = l16; c < cpr; c += 16) {
+      const u32x4 v = xr[c];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) m = amax_bits(v[e], m);
+    }
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 16));
+    int ex = 0;
+    if (m != 0) {
+      const int E = (int)(m >> 7), f = (int)(m & 0x7F);
+      ex = (f <= 96) ? E - 135 : E - 134;
+      ex = max(ex, -127);
+    }
+    const float s = __builtin_ldexpf(1.0f, -ex);
+    uint8_t* out = x8 + r * row_len;
+    for (int c = l16; c < cpr; c += 16) {
+      const u32x4 v = xr[c];
+      u32x2 w;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t lo = v[2 * h], hi = v[2 * h + 1];
+        auto y = [&](uint32_t b) {
+          return fminf(fmaxf(bf16_bits_to_f32(b) * s, -448.0f), 448.0f);
+        };
+        int wd = __builtin_amdgcn_cvt_pk_fp8_f32(y(lo & 0xFFFF), y(lo >> 16), 0, false);
+        wd = __builtin_amdgcn_cvt_pk_fp8_f32(y(hi & 0xFFFF), y(hi >> 16), wd, true);
+        w[h] = (uint32_t)wd;
+      }
+      *reinterpret_cast<u32x2*>(out + c * 8) = w;
+    }
+    if (l16 == 0) e8m0[r] = (uint8_t)(ex + 127);
+  }
+}
+
 }  // namespace dta
 
 using namespace dta;
@@ -311,6 +361,18 @@ extern "C" int fp8_quant_per_tensor(const void* x, int64_t n, void* x8,
   hipLaunchKernelGGL(fp8_cast_kernel, dim3(grid), dim3(256), 0, stream,
                      static_cast<const uint16_t*>(x), n, static_cast<uint8_t*>(x8),
                      descale);
+  return hipGetLastError() == hipSuccess ? DTA_OK : DTA_ELAUNCH;
+}
+
+extern "C" int fp8_quant_rows_pow2(const void* x, int64_t rows, int row_len, void* x8,
+                                   void* e8m0, hipStream_t stream) {
+  if (!x || !x8 || !e8m0 || rows < 1 || row_len < 8 || (row_len & 7)) return DTA_EINVAL;
+  if (!al16(x) || (reinterpret_cast<uintptr_t>(x8) & 7)) return DTA_EALIGN;
+  const int64_t want = (rows + 15) / 16;
+  const unsigned grid = (unsigned)(want < 65536 ? want : 65536);
+  hipLaunchKernelGGL(fp8_rows_pow2_kernel, dim3(grid), dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(x), rows, row_len,
+                     static_cast<uint8_t*>(x8), static_cast<uint8_t*>(e8m0));
   return hipGetLastError() == hipSuccess ? DTA_OK : DTA_ELAUNCH;
 }
 

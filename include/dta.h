@@ -246,6 +246,39 @@ int head_concat(const void* parts, void* out, int P, const int* heads, int B,
 int head_split(const void* x, void* parts, int P, const int* heads, int B,
                int N, int D, hipStream_t stream);
 
+/*
+ * fp8_quant_rows_pow2 -- row-wise dynamic quantisation to E4M3FN with one
+ * power-of-two scale per row (ParaAttention guide, section "fp8
+ * quantization": row-wise scaling as the more accurate alternative to the
+ * per-tensor default). For Q and K a row is one token of one head (row_len
+ * = D):
+ *     e = the smallest integer with amax|row| <= 448 * 2^e, clamped to
+ *         [-127, 127]; e = 0 for an all-zero row
+ *     x8 = e4m3_rne(x * 2^-e)     (the scaling is exact)
+ *     e8m0[row] = e + 127          (OCP E8M0 byte: the scale is 2^(byte-127))
+ * E4M3 keeps 3 mantissa bits in every binade, so a power-of-two scale loses
+ * nothing against amax/448; it only sets the saturation and underflow limits.
+ * x finite bf16 [rows * row_len], 16-byte aligned; x8 uint8 same count,
+ * 8-byte aligned; e8m0 uint8 [rows]. row_len a multiple of 8, rows >= 1.
+ */
+int fp8_quant_rows_pow2(const void* x, int64_t rows, int row_len, void* x8,
+                        void* e8m0, hipStream_t stream);
+
+/*
+ * attn_fwd_fp8_rows -- attn_fwd_fp8 with row-wise power-of-two scales for Q
+ * and K (as fp8_quant_rows_pow2 writes them, one E8M0 byte per token of each
+ * head: q_e8m0 [B,H,Nq], k_e8m0 [B,H,Nkv]) and V per tensor (v_descale,
+ * one device float, as fp8_quant_per_tensor writes it):
+ *     s_ij = scale * 2^(eq_i + ek_j) (Q8_i . K8_j)
+ * The exponents are applied by the fp8 MFMA's operand scales (a per-lane
+ * scale for each key row of K and each query column of Q^T), so they cost
+ * no VALU work. P, O and LSE are as in attn_fwd_fp8.
+ */
+int attn_fwd_fp8_rows(const void* q8, const void* k8, const void* v8,
+                      const void* q_e8m0, const void* k_e8m0,
+                      const float* v_descale, void* o, float* lse, int B, int H,
+                      int Nq, int Nkv, int D, float scale, hipStream_t stream);
+
 /* Bytes of the workspace residual_diff and fp8_quant_per_tensor need. */
 size_t dta_ws_bytes(void);
 

@@ -104,6 +104,20 @@ def test_fbcache_step_validation():
              None) == _lib.DTA_EALIGN
 
 
+def test_fp8_rows_validation():
+    lib = _lib.lib()
+    assert lib.fp8_quant_rows_pow2(GOOD, 0, 128, GOOD, GOOD, None) == _lib.DTA_EINVAL
+    assert lib.fp8_quant_rows_pow2(GOOD, 4, 12, GOOD, GOOD, None) == _lib.DTA_EINVAL   # row_len % 8
+    assert lib.fp8_quant_rows_pow2(GOOD, 4, 128, GOOD, None, None) == _lib.DTA_EINVAL
+    assert lib.fp8_quant_rows_pow2(ODD, 4, 128, GOOD, GOOD, None) == _lib.DTA_EALIGN
+    f = lib.attn_fwd_fp8_rows
+    ok = (GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD)
+    assert f(GOOD, GOOD, GOOD, None, GOOD, GOOD, GOOD, GOOD, 1, 1, 1, 1, 128, 0.1, None) == _lib.DTA_EINVAL
+    assert f(*ok, 1, 1, 1, 0, 128, 0.1, None) == _lib.DTA_EINVAL
+    assert f(*ok, 1, 1, 1, 1, 96, 0.1, None) == _lib.DTA_EUNSUPPORTED
+    assert f(ODD, *ok[1:], 1, 1, 1, 1, 128, 0.1, None) == _lib.DTA_EALIGN
+
+
 def test_layout_validation():
     lib = _lib.lib()
     I = ctypes.c_int

@@ -1,0 +1,134 @@
+"""GPU parity of the row-wise fp8 variant: fp8_quant_rows_pow2 (bit-exact
+codes and E8M0 exponents) and attn_fwd_fp8_rows (against the oracle on the
+dequantised inputs and on the bf16 inputs), through the C ABI."""
+
+import numpy as np
+import pytest
+import torch
+
+import diffusion_transformer_attention_flash_amd as dta
+import oracle
+import workloads
+from helpers import (FP8_O_MEAN_ABS, FP8_REL_L2_VS_BF16, FP8_REL_L2_VS_DEQUANT, LSE_ABS,
+                     rel_l2, to64)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.mark.parametrize("rows,row_len", [(77, 128), (16, 64), (5, 8), (33, 136)])
+def test_quant_rows_bit_exact(rows, row_len):
+    print("CASE rows_pow2 %d x %d" % (rows, row_len), flush=True)
+    g = torch.Generator().manual_seed(rows * 1000 + row_len)
+    mag = torch.exp2(torch.randint(-30, 30, (rows, 1), generator=g).float())
+    x = (torch.randn(rows, row_len, generator=g) * mag)
+    x[0] = 0.0                                           # all-zero row -> exponent 0
+    if rows > 3:
+        x[1, 0] = 448.0 * 2.0 ** 5                       # amax exactly 448 * 2^5
+        x[2, 0] = 448.0 * 2.0 ** -3 * (1 + 2.0 ** -7)    # just above a power
+        x[3, :] = 1e-38                                  # tiny rows clamp at 2^-127
+    x = x.to(torch.bfloat16)
+    x8, e8 = dta.fp8_quant_rows_pow2(x.to(DEV), row_len)
+    torch.cuda.synchronize()
+    codes, e_ref = oracle.quant_rows_pow2(x, row_len)
+    assert np.array_equal(e8.cpu().numpy().ravel(), e_ref)
+    assert np.array_equal(x8.cpu().numpy(), codes)
+
+
+def test_quant_rows_flux_q_bit_exact():
+    print("CASE rows_pow2 flux Q", flush=True)
+    q, _, _ = workloads.workload_qkv("flux_1024", device=DEV)
+    q8, e8 = dta.fp8_quant_rows_pow2(q)
+    torch.cuda.synchronize()
+    codes, e_ref = oracle.quant_rows_pow2(q.cpu(), q.shape[-1])
+    assert np.array_equal(e8.cpu().numpy().ravel(), e_ref)
+    assert np.array_equal(q8.cpu().numpy(), codes)
+
+
+def _rows_path(q, k, v):
+    q8, eq = dta.fp8_quant_rows_pow2(q)
+    k8, ek = dta.fp8_quant_rows_pow2(k)
+    v8, sv = dta.fp8_quant_per_tensor(v)
+    return q8, k8, v8, eq, ek, sv
+
+
+def _check(o8, l8, q, k, v, q8, k8, v8, eq, ek, sv, scale, rows=None, what=""):
+    o_dq, l_dq = oracle.attention_fp8_rows(q8.cpu().numpy(), k8.cpu().numpy(), v8.cpu().numpy(),
+                                           eq.cpu().numpy(), ek.cpu().numpy(), float(sv.item()),
+                                           scale, rows=rows)
+    o_bf, _ = oracle.attention(q.cpu(), k.cpu(), v.cpu(), scale, rows=rows)
+    if rows is not None:
+        rt = torch.from_numpy(rows).to(o8.device)
+        o8, l8 = o8[:, :, rt], l8[:, :, rt]
+    o8, l8 = to64(o8), to64(l8)
+    assert np.isfinite(o8).all() and np.isfinite(l8).all()
+    mean_abs = np.abs(o8 - o_bf).mean()
+    r_bf, r_dq = rel_l2(o8, o_bf), rel_l2(o8, o_dq)
+    e_l = np.abs(l8 - l_dq).max()
+    msg = "%s: O mean-abs %.3e, rel-L2 %.3e (bf16) %.3e (dequant), LSE %.3e" % (
+        what, mean_abs, r_bf, r_dq, e_l)
+    print(msg)
+    assert mean_abs <= FP8_O_MEAN_ABS and r_bf <= FP8_REL_L2_VS_BF16, msg
+    assert r_dq <= FP8_REL_L2_VS_DEQUANT and e_l <= LSE_ABS, msg
+    return r_bf
+
+
+@pytest.mark.parametrize("B,H,Nq,Nkv,D", [(1, 2, 300, 300, 128), (1, 3, 200, 131, 64),
+                                          (1, 1, 64, 1, 128), (2, 1, 97, 640, 128)])
+def test_attention_rows_shapes(B, H, Nq, Nkv, D):
+    print("CASE fp8 rows shape", B, H, Nq, Nkv, D, flush=True)
+    q, k, v = workloads.make_qkv(23, B, H, Nq, Nkv, D, device=DEV)
+    q8, k8, v8, eq, ek, sv = _rows_path(q, k, v)
+    o8, l8 = dta.attn_fwd_fp8_rows(q8, k8, v8, eq, ek, sv, D ** -0.5)
+    torch.cuda.synchronize()
+    _check(o8, l8, q, k, v, q8, k8, v8, eq, ek, sv, D ** -0.5, what="fp8 rows")
+
+
+def test_attention_rows_flux_sampled():
+    c = workloads.CONFIGS["flux_1024_fp8"]
+    print("CASE fp8 rows flux", flush=True)
+    q, k, v = workloads.workload_qkv("flux_1024_fp8", device=DEV)
+    q8, k8, v8, eq, ek, sv = _rows_path(q, k, v)
+    o8, l8 = dta.attn_fwd_fp8_rows(q8, k8, v8, eq, ek, sv, c["D"] ** -0.5)
+    torch.cuda.synchronize()
+    rows = workloads.sample_rows(c["config"], c["N"], 256, c["n_text"])
+    _check(o8, l8, q, k, v, q8, k8, v8, eq, ek, sv, c["D"] ** -0.5, rows=rows, what="fp8 rows flux")
+
+
+def test_uniform_exponents_match_per_tensor_bitwise():
+    """With every row exponent equal, the MFMA operand scales 2^(eq+ek) and
+    the per-tensor path's float factor s_q s_k = 2^(eq+ek) give the same
+    logits exactly, so both kernels must agree bit for bit."""
+    B, H, N, D = 1, 2, 250, 128
+    q, k, v = workloads.make_qkv(24, B, H, N, N, D, device=DEV)
+    q8, _ = dta.fp8_quant_rows_pow2(q)
+    k8, _ = dta.fp8_quant_rows_pow2(k)
+    v8, sv = dta.fp8_quant_per_tensor(v)
+    eq = torch.full((B, H, N), 127 - 3, dtype=torch.uint8, device=DEV)
+    ek = torch.full((B, H, N), 127 + 2, dtype=torch.uint8, device=DEV)
+    o_r, l_r = dta.attn_fwd_fp8_rows(q8, k8, v8, eq, ek, sv, D ** -0.5)
+    ds = torch.cat([torch.tensor([2.0 ** -3, 2.0 ** 2], device=DEV), sv])
+    o_t, l_t = dta.attn_fwd_fp8(q8, k8, v8, ds, D ** -0.5)
+    torch.cuda.synchronize()
+    assert torch.equal(o_r, o_t) and torch.equal(l_r, l_t)
+
+
+def test_outlier_tokens_row_wise_beats_per_tensor():
+    B, H, N, D = 1, 2, 256, 128
+    q, k, v = workloads.make_qkv(25, B, H, N, N, D, device=DEV)
+    q = q.float()
+    q[:, :, 7] *= 65536.0
+    q = q.to(torch.bfloat16)
+    scale = D ** -0.5
+    o_ref, _ = oracle.attention(q.cpu(), k.cpu(), v.cpu(), scale)
+    q8, k8, v8, eq, ek, sv = _rows_path(q, k, v)
+    o_r, _ = dta.attn_fwd_fp8_rows(q8, k8, v8, eq, ek, sv, scale)
+    qt, sq = dta.fp8_quant_per_tensor(q)
+    kt, sk = dta.fp8_quant_per_tensor(k)
+    o_t, _ = dta.attn_fwd_fp8(qt, kt, v8, torch.cat([sq, sk, sv]), scale)
+    torch.cuda.synchronize()
+    keep = [i for i in range(N) if i != 7]
+    err_r = rel_l2(to64(o_r)[:, :, keep], o_ref[:, :, keep])
+    err_t = rel_l2(to64(o_t)[:, :, keep], o_ref[:, :, keep])
+    print("outlier token: rel-L2 row-wise %.3e, per-tensor %.3e" % (err_r, err_t))
+    assert err_r <= FP8_REL_L2_VS_BF16 and err_t > 2 * err_r
