@@ -9,13 +9,86 @@
 // HBM-bound scan. One thread owns 8 consecutive dims (16 bytes) of one row,
 // so every load and store is a coalesced 128-bit access; the per-row LSE
 // values are read by the D/8 threads of the row and served by one cache line.
-// Partials are visited four at a time so that several loads are in flight.
+// For up to 8 partials the count is a template argument and every load of a
+// thread is issued before any arithmetic; more partials are visited four at
+// a time. Partials are read once, with non-temporal loads, so that they
+// stream past the caches instead of evicting the caller's working set.
 // attn_merge_into is the two-part, in-place form used after each ring step.
 
 #include "common.h"
 
 namespace dta {
 
+__device__ __forceinline__ u32x4 load_stream(const uint16_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+// Folds partial (x, w) into the accumulator; a weight-0 partial's O is never
+// used (a select, not a multiply by zero), so garbage there cannot turn into
+// NaN.
+__device__ __forceinline__ void merge_acc(float (&acc)[8], const u32x4& x, float w) {
+  const bool live = w > 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float a0 = fmaf(w, bf16_bits_to_f32(x[e] & 0xFFFF), acc[2 * e]);
+    const float a1 = fmaf(w, bf16_bits_to_f32(x[e] >> 16), acc[2 * e + 1]);
+    acc[2 * e] = live ? a0 : acc[2 * e];
+    acc[2 * e + 1] = live ? a1 : acc[2 * e + 1];
+  }
+}
+
+__device__ __forceinline__ void merge_store(uint16_t* o, float* lse, int64_t row, int ch, int D,
+                                            float (&acc)[8], float m, float wsum) {
+  if (m != -INFINITY) {
+    const float inv = 1.0f / wsum;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] *= inv;
+  }
+  u32x4 out;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) out[e] = pack_bf16x2(acc[2 * e], acc[2 * e + 1]);
+  *reinterpret_cast<u32x4*>(o + row * D + ch * 8) = out;
+  if (ch == 0 && lse != nullptr) lse[row] = (m == -INFINITY) ? -INFINITY : m + logf(wsum);
+}
+
+// N partials (1..8): all loads of the thread first, then the arithmetic.
+template <int D, int N>
+__global__ __launch_bounds__(256) void attn_merge_n_kernel(
+    const uint16_t* __restrict__ op, const float* __restrict__ lp,
+    uint16_t* __restrict__ o, float* __restrict__ lse, int64_t rows) {
+  constexpr int kCh = D / 8;
+  const int64_t total = rows * kCh;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t ci = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; ci < total;
+       ci += stride) {
+    const int64_t row = ci / kCh;
+    const int ch = (int)(ci - row * kCh);
+    u32x4 x[N];
+    float l[N];
+#pragma unroll
+    for (int p = 0; p < N; ++p) {
+      x[p] = load_stream(op + ((int64_t)p * rows + row) * D + ch * 8);
+      l[p] = lp[(int64_t)p * rows + row];
+    }
+    float m = -INFINITY;
+#pragma unroll
+    for (int p = 0; p < N; ++p) m = fmaxf(m, l[p]);
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float wsum = 0.f;
+    if (m != -INFINITY) {
+      const float ml2 = m * kLog2e;
+#pragma unroll
+      for (int p = 0; p < N; ++p) {
+        const float w = __builtin_amdgcn_exp2f(fmaf(l[p], kLog2e, -ml2));
+        wsum += w;
+        merge_acc(acc, x[p], w);
+      }
+    }
+    merge_store(o, lse, row, ch, D, acc, m, wsum);
+  }
+}
+
+// Any number of partials, four at a time.
 template <int D>
 __global__ __launch_bounds__(256) void attn_merge_kernel(
     const uint16_t* __restrict__ op, const float* __restrict__ lp, int n,
@@ -39,49 +112,25 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(
         float w[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          x[u] = *reinterpret_cast<const u32x4*>(
-              op + ((int64_t)(p + u) * rows + row) * D + ch * 8);
+          x[u] = load_stream(op + ((int64_t)(p + u) * rows + row) * D + ch * 8);
           w[u] = __builtin_amdgcn_exp2f(
               fmaf(lp[(int64_t)(p + u) * rows + row], kLog2e, -ml2));
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           wsum += w[u];
-          const bool live = w[u] > 0.f;   // a weight-0 partial's O is never used
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float a0 = fmaf(w[u], bf16_bits_to_f32(x[u][e] & 0xFFFF), acc[2 * e]);
-            const float a1 = fmaf(w[u], bf16_bits_to_f32(x[u][e] >> 16), acc[2 * e + 1]);
-            acc[2 * e] = live ? a0 : acc[2 * e];
-            acc[2 * e + 1] = live ? a1 : acc[2 * e + 1];
-          }
+          merge_acc(acc, x[u], w[u]);
         }
       }
       for (; p < n; ++p) {
-        const u32x4 x = *reinterpret_cast<const u32x4*>(
-            op + ((int64_t)p * rows + row) * D + ch * 8);
+        const u32x4 x = load_stream(op + ((int64_t)p * rows + row) * D + ch * 8);
         const float w = __builtin_amdgcn_exp2f(
             fmaf(lp[(int64_t)p * rows + row], kLog2e, -ml2));
         wsum += w;
-        const bool live = w > 0.f;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float a0 = fmaf(w, bf16_bits_to_f32(x[e] & 0xFFFF), acc[2 * e]);
-          const float a1 = fmaf(w, bf16_bits_to_f32(x[e] >> 16), acc[2 * e + 1]);
-          acc[2 * e] = live ? a0 : acc[2 * e];
-          acc[2 * e + 1] = live ? a1 : acc[2 * e + 1];
-        }
+        merge_acc(acc, x, w);
       }
-      const float inv = 1.0f / wsum;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] *= inv;
     }
-    u32x4 out;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) out[e] = pack_bf16x2(acc[2 * e], acc[2 * e + 1]);
-    *reinterpret_cast<u32x4*>(o + row * D + ch * 8) = out;
-    if (ch == 0 && lse != nullptr)
-      lse[row] = (m == -INFINITY) ? -INFINITY : m + logf(wsum);
+    merge_store(o, lse, row, ch, D, acc, m, wsum);
   }
 }
 
@@ -130,6 +179,32 @@ __global__ __launch_bounds__(256) void attn_merge_into_kernel(
   }
 }
 
+template <int D>
+void launch_merge(const void* o_parts, const float* lse_parts, int n, void* o, float* lse,
+                  int64_t rows, unsigned grid, hipStream_t stream) {
+  const uint16_t* op = static_cast<const uint16_t*>(o_parts);
+  uint16_t* out = static_cast<uint16_t*>(o);
+  switch (n) {
+#define DTA_MERGE_N(N)                                                                       \
+  case N:                                                                                    \
+    hipLaunchKernelGGL((attn_merge_n_kernel<D, N>), dim3(grid), dim3(256), 0, stream, op,    \
+                       lse_parts, out, lse, rows);                                           \
+    break;
+    DTA_MERGE_N(1)
+    DTA_MERGE_N(2)
+    DTA_MERGE_N(3)
+    DTA_MERGE_N(4)
+    DTA_MERGE_N(5)
+    DTA_MERGE_N(6)
+    DTA_MERGE_N(7)
+    DTA_MERGE_N(8)
+#undef DTA_MERGE_N
+    default:
+      hipLaunchKernelGGL(attn_merge_kernel<D>, dim3(grid), dim3(256), 0, stream, op, lse_parts,
+                         n, out, lse, rows);
+  }
+}
+
 }  // namespace dta
 
 using namespace dta;
@@ -150,13 +225,9 @@ extern "C" int attn_merge(const void* o_parts, const float* lse_parts,
   const int64_t want = (total + 255) / 256;
   const unsigned grid = (unsigned)(want < 65536 ? want : 65536);
   if (D == 128)
-    hipLaunchKernelGGL(attn_merge_kernel<128>, dim3(grid), dim3(256), 0, stream,
-                       static_cast<const uint16_t*>(o_parts), lse_parts, n_parts,
-                       static_cast<uint16_t*>(o), lse, rows);
+    launch_merge<128>(o_parts, lse_parts, n_parts, o, lse, rows, grid, stream);
   else
-    hipLaunchKernelGGL(attn_merge_kernel<64>, dim3(grid), dim3(256), 0, stream,
-                       static_cast<const uint16_t*>(o_parts), lse_parts, n_parts,
-                       static_cast<uint16_t*>(o), lse, rows);
+    launch_merge<64>(o_parts, lse_parts, n_parts, o, lse, rows, grid, stream);
   return hipGetLastError() == hipSuccess ? DTA_OK : DTA_ELAUNCH;
 }
 
