@@ -60,21 +60,31 @@ def test_flux_eight_uneven_chunks():
     assert np.abs(to64(lse) - lm).max() < 1e-5
 
 
-@pytest.mark.parametrize("n_parts,D", [(1, 128), (3, 64), (5, 128), (9, 64)])
+# Every instantiated partial count (1..8, one kernel each) at both head dims,
+# and the generic kernel (more than 8 partials).
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("n_parts", [1, 2, 3, 4, 5, 6, 7, 8, 9, 12, 13])
 def test_merge_random_partials(n_parts, D):
     print("CASE merge n=%d D=%d" % (n_parts, D), flush=True)
-    g = torch.Generator().manual_seed(100 + n_parts)
+    g = torch.Generator().manual_seed(100 + n_parts + D)
     B, H, Nq = 2, 3, 77
     o_parts = torch.randn((n_parts, B, H, Nq, D), generator=g).to(torch.bfloat16)
     l_parts = (torch.randn((n_parts, B, H, Nq), generator=g) * 5).to(torch.float32)
-    if n_parts > 2:
+    o_dev = o_parts.clone()
+    if n_parts >= 2:
         l_parts[1, 0, 0, :] = -math.inf            # a chunk that saw nothing
-        l_parts[:, 1, 2, 5] = -math.inf            # a row with nothing at all
-    o, lse = dta.attn_merge(o_parts.to(DEV), l_parts.to(DEV))
+        o_dev[1, 0, 0, :] = math.nan               # its O is garbage: weight 0 must not read it
+        o_parts[1, 0, 0, :] = 0.0                  # (the oracle's sum would take 0 * NaN = NaN)
+    l_parts[:, 1, 2, 5] = -math.inf                # a row with nothing at all
+    o_dev[:, 1, 2, 5] = math.nan
+    o_parts[:, 1, 2, 5] = 0.0
+    o, lse = dta.attn_merge(o_dev.to(DEV), l_parts.to(DEV))
     torch.cuda.synchronize()
     om, lm = oracle.merge(o_parts, l_parts)
     fin = np.isfinite(lm)
-    assert np.abs(to64(o) - om).max() < 2e-2
+    d_o = np.abs(to64(o) - om)
+    ulp = np.maximum(np.abs(om), 2.0 ** -126) * 2.0 ** -8     # one bf16 ulp (upper bound)
+    assert (d_o <= ulp + 1e-6).all(), "merge differs from oracle merge by > 1 bf16 ulp"
     np.testing.assert_allclose(to64(lse)[fin], lm[fin], rtol=0, atol=1e-5)
     assert (to64(lse)[~fin] == -np.inf).all()
     assert (to64(o)[~fin] == 0).all()
