@@ -8,16 +8,18 @@
 // * fp8_quant_per_tensor -- per-tensor dynamic E4M3FN quantisation, scale
 //   amax|x|/448 (ParaAttention guide, section "fp8 quantization").
 //
-// Both are HBM-bound scans. A fixed grid of kRedBlocks workgroups strides
-// over the tensor in 16-byte chunks (two chunks per thread per step, so that
-// four 128-bit loads are in flight), reduces in registers, then across the
-// wave and the workgroup, and writes one partial per workgroup to the
-// workspace. A second, one-workgroup kernel combines the partials in a fixed
-// order in float64. The kernel boundary, not a device-scope fence, publishes
-// the partials: on gfx950 such a fence writes back the whole L2 of the XCD,
-// and one per workgroup costs more than the scan itself. The result is
-// independent of scheduling and bitwise reproducible, and the workspace needs
-// no initialisation.
+// The two grid-wide reductions (residual sums, fp8 amax) are HBM-bound scans.
+// A fixed grid of kRedBlocks workgroups strides over the tensor in 16-byte
+// chunks (two chunks per thread per step, so that four 128-bit loads are in
+// flight), reduces in registers, then across the wave and the workgroup, and
+// writes one partial per workgroup to the workspace. The next kernel combines
+// the partials: for the residual sums a one-workgroup kernel, in a fixed
+// order in float64; for the amax every workgroup of the cast kernel, with an
+// integer max (order-free). The kernel boundary, not a device-scope fence,
+// publishes the partials: on gfx950 such a fence writes back the whole L2 of
+// the XCD, and one per workgroup costs more than the scan itself. The results
+// are independent of scheduling and bitwise reproducible, and the workspace
+// needs no initialisation.
 
 #include "common.h"
 
@@ -198,33 +200,38 @@ __global__ __launch_bounds__(256) void amax_kernel(
   }
 }
 
-// One workgroup: maximum of the kRedBlocks partial maxima, then the scale.
-__global__ __launch_bounds__(256) void amax_finish_kernel(
-    const uint32_t* __restrict__ part, float* __restrict__ descale) {
-  __shared__ uint32_t sm[4];
-  uint32_t r = 0;
-  for (int p = threadIdx.x; p < kRedBlocks; p += 256) r = max(r, part[p]);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) r = max(r, (uint32_t)__shfl_xor((int)r, off, 64));
-  if ((threadIdx.x & 63) == 0) sm[threadIdx.x >> 6] = r;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t bm = max(max(sm[0], sm[1]), max(sm[2], sm[3]));
-    const float amax = bf16_bits_to_f32(bm);
-    *descale = (amax == 0.f) ? 1.0f : __fdiv_rn(amax, 448.0f);
-  }
-}
-
 // E4M3FN code of x / s: correctly rounded float32 division, clamp to the
 // finite range, then v_cvt_pk_fp8_f32 (round to nearest even).
 __device__ __forceinline__ float fp8_in(float x, float s) {
   return fminf(fmaxf(__fdiv_rn(x, s), -448.0f), 448.0f);
 }
 
+// Every workgroup first reduces the kRedBlocks partial maxima itself (one
+// 16-byte load per thread, from L2) instead of a one-workgroup finish launch;
+// workgroup 0 publishes the scale for later kernels.
 __global__ __launch_bounds__(256) void fp8_cast_kernel(
     const uint16_t* __restrict__ x, int64_t n, uint8_t* __restrict__ x8,
-    const float* __restrict__ descale) {
-  const float s = *descale;
+    const uint32_t* __restrict__ part, float* __restrict__ descale) {
+  static_assert(kRedBlocks == 4 * 256, "one 16-byte load of partials per thread");
+  __shared__ uint32_t sm[4];
+  __shared__ float s_sh;
+  {
+    const u32x4 pv = reinterpret_cast<const u32x4*>(part)[threadIdx.x];
+    uint32_t r = max(max(pv[0], pv[1]), max(pv[2], pv[3]));
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) r = max(r, (uint32_t)__shfl_xor((int)r, off, 64));
+    if ((threadIdx.x & 63) == 0) sm[threadIdx.x >> 6] = r;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const uint32_t bm = max(max(sm[0], sm[1]), max(sm[2], sm[3]));
+      const float amax = bf16_bits_to_f32(bm);
+      const float sc = (amax == 0.f) ? 1.0f : __fdiv_rn(amax, 448.0f);
+      s_sh = sc;
+      if (blockIdx.x == 0) *descale = sc;
+    }
+    __syncthreads();
+  }
+  const float s = s_sh;
   const int64_t n8 = n >> 3;
   const int64_t stride = (int64_t)gridDim.x * 256;
   const u32x4* x4 = reinterpret_cast<const u32x4*>(x);
@@ -354,12 +361,10 @@ extern "C" int fp8_quant_per_tensor(const void* x, int64_t n, void* x8,
   hipLaunchKernelGGL(amax_kernel, dim3(kRedBlocks), dim3(256), 0, stream,
                      static_cast<const uint16_t*>(x), n, part);
   if (hipGetLastError() != hipSuccess) return DTA_ELAUNCH;
-  hipLaunchKernelGGL(amax_finish_kernel, dim3(1), dim3(256), 0, stream, part, descale);
-  if (hipGetLastError() != hipSuccess) return DTA_ELAUNCH;
   const int64_t want = ((n >> 3) + 255) / 256;
-  const unsigned grid = (unsigned)(want < 1 ? 1 : (want < 8192 ? want : 8192));
+  const unsigned grid = (unsigned)(want < 1 ? 1 : (want < 4096 ? want : 4096));
   hipLaunchKernelGGL(fp8_cast_kernel, dim3(grid), dim3(256), 0, stream,
-                     static_cast<const uint16_t*>(x), n, static_cast<uint8_t*>(x8),
+                     static_cast<const uint16_t*>(x), n, static_cast<uint8_t*>(x8), part,
                      descale);
   return hipGetLastError() == hipSuccess ? DTA_OK : DTA_ELAUNCH;
 }
