@@ -141,14 +141,14 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_fp8_kernel(
       vreg[it] = __builtin_amdgcn_raw_buffer_load_b128(vr, off, 0, 0);
     }
     if constexpr (ROWS) {
-      // Scales of the keys this lane's A rows hold, through a byte-ranged
-      // buffer resource: keys past Nkv read 0 (2^-127) without a branch;
-      // their K rows are zero and their scores are masked anyway.
-      const __amdgpu_buffer_rsrc_t er = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(ke_h + key0), 0, (int)min<int64_t>(Nkv - key0, BN), kBufDword3Fp8);
+      // Scales of the keys this lane's A rows hold. Keys past Nkv read the
+      // last key's scale (clamped address, no branch): their K rows are zero
+      // and their scores are masked, so the value is never used.
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-        sk_next[kb] = (int)__builtin_amdgcn_raw_buffer_load_b8(er, kb * 32 + l32, 0, 0);
+      for (int kb = 0; kb < 2; ++kb) {
+        const int64_t key = min<int64_t>(key0 + kb * 32 + l32, (int64_t)Nkv - 1);
+        sk_next[kb] = (int)ke_h[key];
+      }
     }
   };
   auto store_tile = [&](int buf) {
