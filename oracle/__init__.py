@@ -36,6 +36,9 @@ What it computes, each written from the plain definition (numpy, float64):
 * ``quant_rows_pow2`` / ``attention_fp8_rows`` -- the row-wise variant the
                          same section names as more accurate: one
                          power-of-two scale per token for Q and K.
+* ``attention_fp8_rows_v`` -- the same with V's per-token scale folded into
+                         the probabilities and one power-of-two P scale per
+                         (query, block of ``p_block_ids``).
 
 Every function is pinned by tests in ``tests/test_oracle_pins.py`` against
 mathematics it does not share code with (arbitrary-precision brute force,
@@ -46,11 +49,12 @@ from .attention import attention, merge, softmax_rows
 from .residual import fbcache_step, residual_diff
 from . import layout
 from .fp8 import (E4M3_MAX, e4m3_decode, e4m3_encode, quant_per_tensor, quant_rows_pow2,
-                  attention_fp8_rows,
-                  attention_fp8)
+                  attention_fp8_rows, attention_fp8_rows_v, p_block_ids, pow2_exponent,
+                  quant_p_blocks, attention_fp8)
 
 __all__ = [
     "attention", "merge", "softmax_rows", "residual_diff", "fbcache_step", "layout", "E4M3_MAX",
     "e4m3_decode", "e4m3_encode", "quant_per_tensor", "attention_fp8",
-    "quant_rows_pow2", "attention_fp8_rows",
+    "quant_rows_pow2", "attention_fp8_rows", "attention_fp8_rows_v", "p_block_ids",
+    "pow2_exponent", "quant_p_blocks",
 ]

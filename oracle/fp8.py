@@ -100,6 +100,17 @@ def attention_fp8(q8, k8, v8, descale, scale, rows=None):
     return _attention_p8(q, k, v, scale, rows)
 
 
+def pow2_exponent(amax):
+    """Smallest integer e with amax <= 448 * 2^e, clamped to [-127, 127];
+    0 where amax == 0. Exact: amax = m * 2^k with 0.5 <= m < 1 (frexp) and
+    448 = 0.875 * 2^9, so amax <= 448 * 2^e iff e >= k - 9 when m <= 0.875,
+    else e >= k - 8."""
+    amax = np.asarray(amax, dtype=np.float64)
+    m, k = np.frexp(amax)
+    e = np.where(m <= 0.875, k - 9, k - 8)
+    return np.where(amax == 0, 0, np.clip(e, -127, 127)).astype(np.int64)
+
+
 def quant_rows_pow2(x, row_len):
     """Row-wise dynamic quantisation to E4M3FN with power-of-two scales.
 
@@ -122,10 +133,7 @@ def quant_rows_pow2(x, row_len):
         raise ValueError("row_len must divide the element count")
     rows = x64.reshape(-1, row_len)
     amax = np.abs(rows).max(axis=1)
-    m, k = np.frexp(amax)                     # amax = m * 2^k, 0.5 <= m < 1
-    # 448 = 0.875 * 2^9: amax <= 448 * 2^e  <=>  e >= k - 9 (m <= 0.875) or k - 8
-    e = np.where(m <= 0.875, k - 9, k - 8)
-    e = np.where(amax == 0, 0, np.clip(e, -127, 127)).astype(np.int64)
+    e = pow2_exponent(amax)
     codes = e4m3_encode(rows * np.ldexp(1.0, -e)[:, None])
     return codes.reshape(np.shape(x)), (e + 127).astype(np.uint8)
 
@@ -162,3 +170,77 @@ def _attention_p8(q, k, v, scale, rows):
             o[b, h] = (p8 @ v[b, h]) / (E4M3_MAX * l)
             lse[b, h] = m[:, 0] + np.log(l[:, 0])
     return o, lse
+
+
+def p_block_ids(nkv, tile=64):
+    """Block of each key for the per-block P scales of ``attention_fp8_rows_v``.
+
+    Key j lies in tile j // tile and, inside it, in half ((j % tile) >> 2) & 1:
+    a block is the 32 keys of a 64-key tile that share bit 2 of their index.
+    (The pages leave the P granularity open; this partition is the one whose
+    32 probabilities of one query sit in one lane of the fp8 P.V product, so a
+    block scale is that lane's operand scale. Any fixed partition serves the
+    purpose, finer P scaling; this one is taken and pinned.)
+    """
+    j = np.arange(int(nkv))
+    return 2 * (j // tile) + (((j % tile) >> 2) & 1)
+
+
+def quant_p_blocks(pv, blocks):
+    """E4M3 codes of the probabilities pv [rows, Nkv] with one power-of-two
+    scale per (row, block): 2^e with e = pow2_exponent(max of the block), so
+    the block's largest value lands in [224, 448]. Returns (codes, e) with e
+    of shape [rows, n_blocks]."""
+    pv = np.asarray(pv, dtype=np.float64)
+    blocks = np.asarray(blocks)
+    nb = int(blocks.max()) + 1
+    e = np.zeros((pv.shape[0], nb), dtype=np.int64)
+    for b in range(nb):
+        idx = np.nonzero(blocks == b)[0]
+        e[:, b] = pow2_exponent(pv[:, idx].max(axis=1))
+    codes = e4m3_encode(pv * np.ldexp(1.0, -e[:, blocks]))
+    return codes, e
+
+
+def attention_fp8_rows_v(q8, k8, v8, q_e8m0, k_e8m0, v_e8m0, scale, rows=None):
+    """Row-wise fp8 attention with per-token scales for Q, K and V and
+    per-block scales for P (ParaAttention guide, section "fp8 quantization":
+    row-wise scaling as the more accurate option).
+
+    Q, K and V are E4M3 codes with one power-of-two scale per token (E8M0
+    bytes [B,H,N]). With p = exp(s - m) as in ``attention_fp8``, V's scale is
+    folded into the probabilities, pv_j = p_j * 2^(ev_j - 127), which are
+    quantised to E4M3 with one power-of-two scale per (query, block of
+    ``p_block_ids``) before the product with V's codes:
+    O = sum_j P^_j * v8_j / sum_j p_j, LSE = m + ln sum_j p_j, where P^ is the
+    dequantised pv. A block shares one scale, so inside a block pv values
+    more than E4M3's span (about 2^17) below the block maximum round to zero;
+    a per-tensor V scale has the same limit over the whole tensor.
+    """
+    q = e4m3_decode(np.asarray(q8)) * np.ldexp(1.0, np.asarray(q_e8m0, dtype=np.int64) - 127)[..., None]
+    k = e4m3_decode(np.asarray(k8)) * np.ldexp(1.0, np.asarray(k_e8m0, dtype=np.int64) - 127)[..., None]
+    vq = e4m3_decode(np.asarray(v8))
+    ev = np.asarray(v_e8m0, dtype=np.int64) - 127
+    B, H, Nq, D = q.shape
+    nkv = k.shape[2]
+    if nkv < 1:
+        raise ValueError("Nkv must be >= 1")
+    if rows is not None:
+        q = q[:, :, np.asarray(rows, dtype=np.int64), :]
+    nq = q.shape[2]
+    blocks = p_block_ids(nkv)
+    o = np.empty((B, H, nq, D), dtype=np.float64)
+    lse = np.empty((B, H, nq), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            s = float(scale) * (q[b, h] @ k[b, h].T)
+            m = s.max(axis=1, keepdims=True)
+            p = np.exp(s - m)
+            l = p.sum(axis=1, keepdims=True)
+            pv = p * np.ldexp(1.0, ev[b, h])[None, :]
+            codes, e = quant_p_blocks(pv, blocks)
+            pq = e4m3_decode(codes) * np.ldexp(1.0, e[:, blocks])
+            o[b, h] = (pq @ vq[b, h]) / l
+            lse[b, h] = m[:, 0] + np.log(l[:, 0])
+    return o, lse
+

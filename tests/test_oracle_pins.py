@@ -623,3 +623,128 @@ def test_rows_pow2_attention_beats_per_tensor_on_outlier_tokens():
     err_t = np.linalg.norm((o_t - o_ref)[:, :, rows]) / np.linalg.norm(o_ref[:, :, rows])
     err_r = np.linalg.norm((o_r - o_ref)[:, :, rows]) / np.linalg.norm(o_ref[:, :, rows])
     assert err_r < 0.08 and err_t > 3 * err_r, (err_r, err_t)
+
+
+# ---- per-token V and per-block P scales (attention_fp8_rows_v) ----
+
+def test_p_block_partition():
+    # Keys of block 0 in the first 64-key tile, written out: the 4-key groups
+    # 0-3, 8-11, ..., 56-59 (bit 2 of the index clear).
+    first = [0, 1, 2, 3, 8, 9, 10, 11, 16, 17, 18, 19, 24, 25, 26, 27,
+             32, 33, 34, 35, 40, 41, 42, 43, 48, 49, 50, 51, 56, 57, 58, 59]
+    for nkv in (1, 5, 64, 100, 128, 4608):
+        blk = oracle.p_block_ids(nkv)
+        assert blk.shape == (nkv,) and blk.min() == 0
+        counts = np.bincount(blk)
+        assert counts.sum() == nkv
+        full = nkv // 64
+        assert (counts[:2 * full] == 32).all()
+        for t in range(full):
+            assert np.array_equal(np.nonzero(blk == 2 * t)[0], 64 * t + np.array(first))
+            assert np.array_equal(np.nonzero(blk == 2 * t + 1)[0], 64 * t + np.array(first) + 4)
+
+
+def test_p_block_exponent_is_minimal_and_codes_match_torch():
+    rng = np.random.default_rng(31)
+    n = 200
+    # float32-exact values spread over many binades, one row all zero, one zero tile
+    pv = (rng.random((7, n)).astype(np.float32).astype(np.float64)
+          * np.exp2(rng.integers(-40, 20, size=(7, 1)).astype(np.float64)))
+    pv[3, :] = 0.0
+    pv[4, 64:128] = 0.0
+    blk = oracle.p_block_ids(n)
+    codes, e = oracle.quant_p_blocks(pv, blk)
+    for r in range(pv.shape[0]):
+        for b in range(e.shape[1]):
+            amax = pv[r, blk == b].max()
+            if amax == 0:
+                assert e[r, b] == 0
+                continue
+            assert amax <= 448.0 * 2.0 ** e[r, b]
+            assert amax > 448.0 * 2.0 ** (e[r, b] - 1)
+    scaled = torch.from_numpy(pv * np.exp2(-e[:, blk]).astype(np.float64)).to(torch.float32)
+    ref = scaled.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(codes, ref)
+
+
+def test_rows_v_uniform_scores_give_the_mean_of_v():
+    """All scores equal (Q = 0): every p is 1, each block's pv are powers of
+    two that E4M3 holds exactly after the block scale, so O is the plain mean
+    of the dequantised V rows and LSE = ln N."""
+    B, H, N, D = 1, 2, 150, 32
+    _, k, v = workloads.make_qkv(17, B, H, N, N, D)
+    v = (v.float() * torch.exp2(torch.randint(-6, 7, (B, H, N, 1),
+                                              generator=torch.Generator().manual_seed(4)).float())
+         ).to(torch.bfloat16)
+    q = torch.zeros(B, H, N, D, dtype=torch.bfloat16)
+    qr, eq = oracle.quant_rows_pow2(q, D)
+    kr, ek = oracle.quant_rows_pow2(k, D)
+    vr, ev = oracle.quant_rows_pow2(v, D)
+    o, lse = oracle.attention_fp8_rows_v(qr, kr, vr, eq.reshape(B, H, N), ek.reshape(B, H, N),
+                                         ev.reshape(B, H, N), 0.125)
+    v_deq = oracle.e4m3_decode(vr) * np.exp2(ev.reshape(B, H, N, 1).astype(np.float64) - 127)
+    mean = v_deq.mean(axis=2, keepdims=True)
+    assert np.allclose(o, np.broadcast_to(mean, o.shape), rtol=1e-12, atol=1e-12)
+    assert np.allclose(lse, math.log(N), rtol=0, atol=1e-12)
+
+
+def test_rows_v_beats_per_tensor_v_on_an_outlier_value_token():
+    """A value token x 2^16 (in 8 of 64 dims) sets the per-tensor V scale and
+    pushes every other token's V into E4M3's subnormals; per-token V scales
+    folded into the block-scaled P do not (the outlier shares its P block
+    with 31 keys, and 2^16 is inside E4M3's 2^17 span). Measured on the dims
+    the outlier does not touch."""
+    B, H, N, D = 1, 2, 96, 64
+    q, k, v = workloads.make_qkv(13, B, H, N, N, D)
+    v = v.float()
+    v[:, :, 7, :8] *= 65536.0
+    v[:, :, 7, 8:] = 0.0
+    v = v.to(torch.bfloat16)
+    scale = D ** -0.5
+    o_ref, _ = oracle.attention(q, k, v, scale)
+    qr, eq = oracle.quant_rows_pow2(q, D)
+    kr, ek = oracle.quant_rows_pow2(k, D)
+    vt, sv = oracle.quant_per_tensor(v)
+    vr, ev = oracle.quant_rows_pow2(v, D)
+    sh = (B, H, N)
+    o_t, _ = oracle.attention_fp8_rows(qr, kr, vt, eq.reshape(sh), ek.reshape(sh), sv, scale)
+    o_v, _ = oracle.attention_fp8_rows_v(qr, kr, vr, eq.reshape(sh), ek.reshape(sh),
+                                         ev.reshape(sh), scale)
+    d = slice(8, None)
+    ref = np.linalg.norm(o_ref[..., d])
+    err_t = np.linalg.norm((o_t - o_ref)[..., d]) / ref
+    err_v = np.linalg.norm((o_v - o_ref)[..., d]) / ref
+    assert err_v < 0.08 and err_t > 1.6 * err_v, (err_v, err_t)
+
+
+def test_rows_v_keeps_a_diffuse_tail_that_x448_p_scaling_flushes():
+    """One query over 60000 keys: a peak key and a tail at p ~ 1e-6 each
+    (several % of the mass). 448 p < 2^-10 rounds to zero in E4M3, so the
+    x448 P scaling loses the tail; per-block P scales keep it."""
+    N, D = 60000, 16
+    scale = 1.0
+    g = torch.Generator().manual_seed(23)
+    q = torch.zeros(1, 1, 1, D)
+    q[..., 0] = 4.0
+    k = torch.zeros(1, 1, N, D)
+    k[0, 0, 0, 0] = 0.0
+    k[0, 0, 1:, 0] = -math.log(1e6) / 4.0 * (1.0 + 0.01 * torch.randn(N - 1, generator=g))
+    v = 1.0 + torch.rand(1, 1, N, D, generator=g)
+    v[0, 0, 0] = 0.0                                       # the peak adds nothing to O
+    q, k, v = (t.to(torch.bfloat16) for t in (q, k, v))
+    qr, eq = oracle.quant_rows_pow2(q, D)
+    kr, ek = oracle.quant_rows_pow2(k, D)
+    vt, sv = oracle.quant_per_tensor(v)
+    vr, ev = oracle.quant_rows_pow2(v, D)
+    # Reference: exact attention on the dequantised inputs, so that only the
+    # handling of P differs (fp8 Q/K move scores near -13.8 by up to ~0.9).
+    deq = [oracle.e4m3_decode(c) * np.exp2(e.reshape(sh + (1,)).astype(np.float64) - 127)
+           for c, e, sh in ((qr, eq, (1, 1, 1)), (kr, ek, (1, 1, N)), (vr, ev, (1, 1, N)))]
+    o_ref, _ = oracle.attention(*deq, scale)
+    o_t, _ = oracle.attention_fp8_rows(qr, kr, vt, eq.reshape(1, 1, 1), ek.reshape(1, 1, N), sv, scale)
+    o_v, _ = oracle.attention_fp8_rows_v(qr, kr, vr, eq.reshape(1, 1, 1), ek.reshape(1, 1, N),
+                                         ev.reshape(1, 1, N), scale)
+    ref = np.linalg.norm(o_ref)
+    err_t = np.linalg.norm(o_t - o_ref) / ref
+    err_v = np.linalg.norm(o_v - o_ref) / ref
+    assert err_t > 0.9 and err_v < 0.1, (err_v, err_t)
