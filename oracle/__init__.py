@@ -38,7 +38,7 @@ What it computes, each written from the plain definition (numpy, float64):
                          power-of-two scale per token for Q and K.
 * ``attention_fp8_rows_v`` -- the same with V's per-token scale folded into
                          the probabilities and one power-of-two P scale per
-                         (query, block of ``p_block_ids``).
+                         (query, 32 consecutive keys).
 
 Every function is pinned by tests in ``tests/test_oracle_pins.py`` against
 mathematics it does not share code with (arbitrary-precision brute force,

@@ -172,18 +172,14 @@ def _attention_p8(q, k, v, scale, rows):
     return o, lse
 
 
-def p_block_ids(nkv, tile=64):
-    """Block of each key for the per-block P scales of ``attention_fp8_rows_v``.
-
-    Key j lies in tile j // tile and, inside it, in half ((j % tile) >> 2) & 1:
-    a block is the 32 keys of a 64-key tile that share bit 2 of their index.
-    (The pages leave the P granularity open; this partition is the one whose
-    32 probabilities of one query sit in one lane of the fp8 P.V product, so a
-    block scale is that lane's operand scale. Any fixed partition serves the
-    purpose, finer P scaling; this one is taken and pinned.)
+def p_block_ids(nkv, block=32):
+    """Block of each key for the per-block P scales of ``attention_fp8_rows_v``:
+    32 consecutive keys, key j in block j // 32. (The pages leave the P
+    granularity open. gfx950's fp8 MFMA applies one operand scale to each 32
+    consecutive k of a row or column, measured with single-byte probes, so a
+    block of 32 consecutive keys is one operand scale of the P.V product.)
     """
-    j = np.arange(int(nkv))
-    return 2 * (j // tile) + (((j % tile) >> 2) & 1)
+    return np.arange(int(nkv)) // block
 
 
 def quant_p_blocks(pv, blocks):
@@ -210,8 +206,8 @@ def attention_fp8_rows_v(q8, k8, v8, q_e8m0, k_e8m0, v_e8m0, scale, rows=None):
     Q, K and V are E4M3 codes with one power-of-two scale per token (E8M0
     bytes [B,H,N]). With p = exp(s - m) as in ``attention_fp8``, V's scale is
     folded into the probabilities, pv_j = p_j * 2^(ev_j - 127), which are
-    quantised to E4M3 with one power-of-two scale per (query, block of
-    ``p_block_ids``) before the product with V's codes:
+    quantised to E4M3 with one power-of-two scale per (query, block of 32
+    consecutive keys, ``p_block_ids``) before the product with V's codes:
     O = sum_j P^_j * v8_j / sum_j p_j, LSE = m + ln sum_j p_j, where P^ is the
     dequantised pv. A block shares one scale, so inside a block pv values
     more than E4M3's span (about 2^17) below the block maximum round to zero;
