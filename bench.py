@@ -316,19 +316,26 @@ def main():
         legs["fbcache_step"] = fb
         del hid, cac
 
-    # Row-wise fp8 (per-token power-of-two Q/K scales applied by the MFMA
-    # operand scales, per-tensor V) at the FLUX shape, outside the step.
+    # Row-wise fp8 at the FLUX shape, outside the step: per-token power-of-two
+    # Q/K scales applied by the MFMA operand scales with per-tensor V
+    # (attn_fwd_fp8_rows), and with per-token V scales folded into per-block
+    # scaled P (attn_fwd_fp8_rows_v).
     if "fp8" in legs_on:
         rq8 = torch.empty_like(q8)
         rk8 = torch.empty_like(q8)
+        rv8 = torch.empty_like(q8)
         req = torch.empty((B, H, N), dtype=torch.uint8, device=dev)
         rek = torch.empty_like(req)
+        rev = torch.empty_like(req)
         ro = torch.empty_like(q)
         rl = torch.empty_like(lse)
+        dta.fp8_quant_rows_pow2(v, x8=rv8, e8m0=rev)
         rows_legs = {}
         for name, fn in (
                 ("quant_rows_q_and_k", lambda: (dta.fp8_quant_rows_pow2(q, x8=rq8, e8m0=req),
                                                 dta.fp8_quant_rows_pow2(k, x8=rk8, e8m0=rek))),
+                ("attn_fwd_fp8_rows_v", lambda: dta.attn_fwd_fp8_rows_v(rq8, rk8, rv8, req, rek, rev,
+                                                                        scale, o=ro, lse=rl)),
                 ("attn_fwd_fp8_rows", lambda: dta.attn_fwd_fp8_rows(rq8, rk8, v8, req, rek, ds[2:3],
                                                                     scale, o=ro, lse=rl))):
             for _ in range(3):
@@ -344,12 +351,13 @@ def main():
             rows_legs[name] = {"ms": ms}
         qb = 2 * (q.numel() * 2 + q.numel() + B * H * N)
         rows_legs["quant_rows_q_and_k"]["GB/s"] = qb / (rows_legs["quant_rows_q_and_k"]["ms"] * 1e-3) / 1e9
-        tf = flop_full / (rows_legs["attn_fwd_fp8_rows"]["ms"] * 1e-3) / 1e12
-        rows_legs["attn_fwd_fp8_rows"]["TFLOP/s"] = tf
-        rows_legs["attn_fwd_fp8_rows"]["frac_fp8_peak"] = tf / PEAK_FP8_TFLOPS
+        for kname in ("attn_fwd_fp8_rows", "attn_fwd_fp8_rows_v"):
+            tf = flop_full / (rows_legs[kname]["ms"] * 1e-3) / 1e12
+            rows_legs[kname]["TFLOP/s"] = tf
+            rows_legs[kname]["frac_fp8_peak"] = tf / PEAK_FP8_TFLOPS
         rows_legs["in_step"] = False
         legs["fp8_rows"] = rows_legs
-        del rq8, rk8, req, rek, ro, rl
+        del rq8, rk8, rv8, req, rek, rev, ro, rl
 
     # Layout kernels of context parallelism at the FLUX tensor size (P = 8):
     # Ulysses' head split of Q for the all-to-all, and the token concat of 8

@@ -20,7 +20,7 @@ from ._lib import DtaError  # noqa: F401
 
 __all__ = ["attn_fwd", "attn_merge", "attn_fwd_accum", "attn_merge_into", "residual_diff",
            "fbcache_step", "seq_concat", "seq_split", "head_concat", "head_split",
-           "fp8_quant_rows_pow2", "attn_fwd_fp8_rows",
+           "fp8_quant_rows_pow2", "attn_fwd_fp8_rows", "attn_fwd_fp8_rows_v",
            "fp8_quant_per_tensor",
            "attn_fwd_fp8", "workspace", "DtaError"]
 
@@ -364,4 +364,32 @@ def attn_fwd_fp8_rows(q8, k8, v8, q_e8m0, k_e8m0, v_descale, scale=None, o=None,
                                       _ptr(v_descale), _ptr(o), _ptr(lse), B, H, Nq, Nkv, D,
                                       float(scale), ctypes_ptr(_stream(q8)))
     _lib.check("attn_fwd_fp8_rows", st)
+    return o, lse
+
+
+def attn_fwd_fp8_rows_v(q8, k8, v8, q_e8m0, k_e8m0, v_e8m0, scale=None, o=None, lse=None):
+    """fp8 attention with per-token power-of-two scales for Q, K and V (E8M0
+    bytes [B,H,N]) and per-block power-of-two P scales."""
+    _need(q8, "q8", torch.uint8, 4)
+    _need(k8, "k8", torch.uint8, 4)
+    _need(v8, "v8", torch.uint8, 4)
+    _need(q_e8m0, "q_e8m0", torch.uint8)
+    _need(k_e8m0, "k_e8m0", torch.uint8)
+    _need(v_e8m0, "v_e8m0", torch.uint8)
+    B, H, Nq, D = q8.shape
+    Nkv = k8.shape[2]
+    if tuple(k8.shape) != (B, H, Nkv, D) or tuple(v8.shape) != (B, H, Nkv, D):
+        raise ValueError("shape mismatch")
+    if q_e8m0.numel() != B * H * Nq or k_e8m0.numel() != B * H * Nkv or v_e8m0.numel() != B * H * Nkv:
+        raise ValueError("q_e8m0 / k_e8m0 / v_e8m0 must hold one byte per token of each head")
+    if scale is None:
+        scale = D ** -0.5
+    if o is None:
+        o = torch.empty((B, H, Nq, D), dtype=torch.bfloat16, device=q8.device)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q8.device)
+    st = _lib.lib().attn_fwd_fp8_rows_v(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(q_e8m0), _ptr(k_e8m0),
+                                        _ptr(v_e8m0), _ptr(o), _ptr(lse), B, H, Nq, Nkv, D,
+                                        float(scale), ctypes_ptr(_stream(q8)))
+    _lib.check("attn_fwd_fp8_rows_v", st)
     return o, lse

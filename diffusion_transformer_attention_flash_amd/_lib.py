@@ -27,6 +27,7 @@ SIGNATURES = {
     "attn_fwd_fp8": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P]),
     "fp8_quant_rows_pow2": (_I, [_P, _I64, _I, _P, _P, _P]),
     "attn_fwd_fp8_rows": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P]),
+    "attn_fwd_fp8_rows_v": (_I, [_P] * 8 + [_I] * 5 + [_F, _P]),
     "seq_concat": (_I, [_P, _P, _I, _P, _P, _I, _I, _I, _P]),
     "seq_split": (_I, [_P, _P, _I, _P, _P, _I, _I, _I, _P]),
     "head_concat": (_I, [_P, _P, _I, _P, _I, _I, _I, _P]),

@@ -77,20 +77,33 @@ __device__ __forceinline__ i32x8 cat8(u32x4 lo, u32x4 hi) {
                (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
 }
 
-// ROWS: Q and K carry one power-of-two scale per token (E8M0 bytes q_e8,
-// k_e8); the score MFMA applies them through its operand scales (A row =
-// key, B column = query), and descale[0] is V's per-tensor scale.
-template <int D, int NW, bool ROWS>
+// MODE 0: per-tensor scales descale[0..2] for Q, K, V.
+// MODE 1 (rows): Q and K carry one power-of-two scale per token (E8M0 bytes
+// q_e8, k_e8); the score MFMA applies them through its operand scales (A row
+// = key, B column = query), and descale[0] is V's per-tensor scale.
+// MODE 2 (rows_v): as MODE 1, and V carries one power-of-two scale per token
+// (E8M0 bytes v_e8). V's scale is folded into the probabilities,
+// pv = p * 2^(ev - 127), which are quantised with one power-of-two scale per
+// (query, block of 32 consecutive keys). The fp8 MFMA applies one operand
+// scale to each 32 consecutive k of a column, taken from lane half
+// kb of that column (measured: bytes 0-15 of every lane are scaled by the
+// lower lanes' scale, bytes 16-31 by the upper lanes'), and a lane's P bytes
+// 0-15 / 16-31 are its keys of block kb = 0 / 1. So each block's max is
+// reduced over the lane pair (l, l ^ 32) and lane half g supplies block g's
+// scale to the P.V MFMA.
+template <int D, int NW, int MODE>
 __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_fp8_kernel(
     const uint8_t* __restrict__ q, const uint8_t* __restrict__ k,
     const uint8_t* __restrict__ v, const float* __restrict__ descale,
     const uint8_t* __restrict__ q_e8, const uint8_t* __restrict__ k_e8,
-    uint16_t* __restrict__ o, float* __restrict__ lse, int Nq, int Nkv,
-    float scale, int n_qt) {
+    const uint8_t* __restrict__ v_e8, uint16_t* __restrict__ o, float* __restrict__ lse,
+    int Nq, int Nkv, float scale, int n_qt) {
+  constexpr bool ROWS = MODE >= 1;
   using C = Fp8Cfg<D, NW>;
   constexpr int BN = C::kBN;
   __shared__ __attribute__((aligned(16))) uint8_t ks[2][BN * C::kKS];
   __shared__ __attribute__((aligned(16))) uint8_t vs[2][BN * C::kVS];
+  __shared__ __attribute__((aligned(16))) uint8_t ves[2][MODE == 2 ? BN : 4];   // V exponents
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -103,12 +116,14 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_fp8_kernel(
   const int row = qt * C::kBM + wave * 32 + l32;
 
   const float s_q = ROWS ? 1.0f : descale[0], s_k = ROWS ? 1.0f : descale[1];
-  const float s_v = ROWS ? descale[0] : descale[2];
+  const float s_v = MODE == 2 ? 1.0f : (ROWS ? descale[0] : descale[2]);
   const float c = scale * s_q * s_k * kLog2e;
   // E8M0 operand scales of the score MFMA (127 = 2^0).
   const int sq_e = (ROWS && row < Nq) ? (int)q_e8[(int64_t)bh * Nq + row] : 127;
   const uint8_t* ke_h = ROWS ? k_e8 + (int64_t)bh * Nkv : nullptr;
+  const uint8_t* ve_h = MODE == 2 ? v_e8 + (int64_t)bh * Nkv : nullptr;
   int sk_next[2] = {127, 127};
+  int ve_next = 127;                     // V exponent byte of key tid (tid < BN)
 
   // Q^T operand: 32 bytes (dims kk*64 + 32g .. +31) per 64-dim step.
   i32x8 qr[D / 64];
@@ -150,6 +165,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_fp8_kernel(
         sk_next[kb] = (int)ke_h[key];
       }
     }
+    if constexpr (MODE == 2) {
+      // Same clamp: a key past Nkv has a zero V row and zero probability.
+      if (tid < BN) ve_next = (int)ve_h[min<int64_t>(key0 + tid, (int64_t)Nkv - 1)];
+    }
   };
   auto store_tile = [&](int buf) {
 #pragma unroll
@@ -157,6 +176,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_fp8_kernel(
       const int r = st_r + it * kRowsPerIt;
       *reinterpret_cast<u32x4*>(&ks[buf][r * C::kKS + st_c * 16]) = kreg[it];
       *reinterpret_cast<u32x4*>(&vs[buf][v8_row(r) * C::kVS + st_c * 16]) = vreg[it];
+    }
+    if constexpr (MODE == 2) {
+      if (tid < BN) ves[buf][tid] = (uint8_t)ve_next;
     }
   };
 
@@ -221,29 +243,89 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_fp8_kernel(
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
     }
-    const float m448 = m_run - kLog2PScale;
-    float rs = 0.f;
     i32x8 pb;
+    int sb_e = 127;                      // P.V MFMA B operand scale (E8M0)
+    if constexpr (MODE != 2) {
+      const float m448 = m_run - kLog2PScale;
+      float rs = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        float p[4];
+        for (int w = 0; w < 4; ++w) {
+          float p[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int r = 4 * w + u;
-          p[u] = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c, -m448));
-          if constexpr (MASK) {
-            if (kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3) >= key_lim) p[u] = 0.f;
+          for (int u = 0; u < 4; ++u) {
+            const int r = 4 * w + u;
+            p[u] = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c, -m448));
+            if constexpr (MASK) {
+              if (kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3) >= key_lim) p[u] = 0.f;
+            }
+            rs += p[u];
           }
-          rs += p[u];
+          int wd = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+          wd = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], wd, true);
+          pb[kb * 4 + w] = wd;
+          asm volatile("" : "+v"(rs));
         }
-        int wd = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
-        wd = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], wd, true);
-        pb[kb * 4 + w] = wd;
-        asm volatile("" : "+v"(rs));
+      l_run += rs;
+    } else {
+      // p = 2^(s c - m_run) in (0, 2^kTau8]; l_run sums p. pv = p 2^(ev-127)
+      // for this lane's keys kb*32 + 8w + 4g + u (4 consecutive exponent
+      // bytes per (kb, w): one aligned LDS word).
+      const uint8_t* vte = ves[buf];
+      float pv[2][16];
+      float rs = 0.f, bmax[2] = {0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t ew = *reinterpret_cast<const uint32_t*>(vte + kb * 32 + 8 * w + 4 * g);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int r = 4 * w + u;
+            float p = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c, -m_run));
+            if constexpr (MASK) {
+              if (kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3) >= key_lim) p = 0.f;
+            }
+            rs += p;
+            const int ev = (int)((ew >> (8 * u)) & 0xFFu) - 127;
+            pv[kb][r] = __builtin_amdgcn_ldexpf(p, ev);
+            bmax[kb] = fmaxf(bmax[kb], pv[kb][r]);
+          }
+          asm volatile("" : "+v"(rs));
+        }
+      l_run += rs;
+      // Block exponent: the smallest e with bmax <= 448 * 2^e, read off the
+      // float32 bits of bmax = (1 + f/2^23) 2^(E-127): 448 * 2^e = 1.75 *
+      // 2^(8+e), so e = E - 135 when 1 + f/2^23 <= 1.75, else E - 134.
+      // Clamped to [-126, 127] (a block below 448 * 2^-127 still fits
+      // 2^-126 exactly, and keeps the conversion scale a normal float).
+      int ebk[2];
+      float sck[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const float bm = xhalf_max8(bmax[kb]);          // the block's 32 keys
+        const uint32_t bb = __float_as_uint(bm);
+        const int E = (int)(bb >> 23);
+        int eb = (bb & 0x7FFFFFu) <= 0x600000u ? E - 135 : E - 134;
+        eb = bm > 0.f ? max(min(eb, 127), -126) : 0;
+        ebk[kb] = eb;
+        sck[kb] = __builtin_amdgcn_ldexpf(1.0f, eb);
       }
-    l_run += rs;
+      sb_e = (g == 0 ? ebk[0] : ebk[1]) + 127;
+      typedef short s16x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          // pv / 2^eb <= 448: the unsaturated scaled conversion cannot overflow.
+          s16x2 wd = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(
+              s16x2{0, 0}, pv[kb][4 * w], pv[kb][4 * w + 1], sck[kb], false);
+          wd = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(wd, pv[kb][4 * w + 2], pv[kb][4 * w + 3],
+                                                        sck[kb], true);
+          pb[kb * 4 + w] = __builtin_bit_cast(int, wd);
+        }
+    }
 
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
@@ -254,8 +336,12 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_fp8_kernel(
             (lds_i32x2*)(vt + v_base + 8 * a * C::kVS + db * 32));
       const i32x8 av = {part[0][0], part[0][1], part[1][0], part[1][1],
                         part[2][0], part[2][1], part[3][0], part[3][1]};
-      oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, pb, oacc[db], 0, 0, 0, 0,
-                                                                  0, 0);
+      if constexpr (MODE == 2)
+        oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, pb, oacc[db], 0, 0, 0,
+                                                                    127, 0, sb_e);
+      else
+        oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, pb, oacc[db], 0, 0, 0, 0,
+                                                                    0, 0);
     }
 
     if (has_next) store_tile(buf ^ 1);
@@ -278,7 +364,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_fp8_kernel(
       tile(j, B0{}, std::true_type{});
   }
 
-  // l_run holds 108 l; O = s_v * acc / (108 l).
+  // MODE 0/1: l_run holds 108 l and O = s_v * acc / (108 l). MODE 2: l_run
+  // holds l and O = acc / l (V's scale is in P).
   const float lt = xhalf_sum8(l_run);
   const float f = s_v / lt;
   if (row < Nq) {
@@ -293,25 +380,28 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_fp8_kernel(
         *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * jj + 4 * g) = w;
       }
     if (g == 0 && lse != nullptr)
-      lse[(int64_t)bh * Nq + row] = (m_run + log2f(lt) - kLog2PScale) * kLn2;
+      lse[(int64_t)bh * Nq + row] =
+          (m_run + log2f(lt) - (MODE == 2 ? 0.0f : kLog2PScale)) * kLn2;
   }
 }
 
-template <int D, int NW, bool ROWS>
+template <int D, int NW, int MODE>
 static int launch_fp8(const void* q8, const void* k8, const void* v8,
-                      const float* descale, const void* q_e8, const void* k_e8, void* o,
+                      const float* descale, const void* q_e8, const void* k_e8,
+                      const void* v_e8, void* o,
                       float* lse, int B, int H, int Nq, int Nkv, float scale,
                       hipStream_t stream) {
   using C = Fp8Cfg<D, NW>;
   const int n_qt = (Nq + C::kBM - 1) / C::kBM;
   const int64_t grid = (int64_t)n_qt * B * H;
   if (grid > 0x7FFFFFFF) return DTA_EUNSUPPORTED;
-  hipLaunchKernelGGL((attn_fwd_fp8_kernel<D, NW, ROWS>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((attn_fwd_fp8_kernel<D, NW, MODE>), dim3((unsigned)grid),
                      dim3(C::kThreads), 0, stream,
                      static_cast<const uint8_t*>(q8), static_cast<const uint8_t*>(k8),
                      static_cast<const uint8_t*>(v8), descale,
                      static_cast<const uint8_t*>(q_e8), static_cast<const uint8_t*>(k_e8),
-                     static_cast<uint16_t*>(o), lse, Nq, Nkv, scale, n_qt);
+                     static_cast<const uint8_t*>(v_e8), static_cast<uint16_t*>(o), lse, Nq, Nkv,
+                     scale, n_qt);
   return hipGetLastError() == hipSuccess ? DTA_OK : DTA_ELAUNCH;
 }
 
@@ -334,10 +424,10 @@ extern "C" int attn_fwd_fp8(const void* q8, const void* k8, const void* v8,
       (lse && !al(lse, 4)))
     return DTA_EALIGN;
   if (D == 128)
-    return launch_fp8<128, 4, false>(q8, k8, v8, descale, nullptr, nullptr, o, lse, B, H, Nq,
-                                     Nkv, scale, stream);
-  return launch_fp8<64, 4, false>(q8, k8, v8, descale, nullptr, nullptr, o, lse, B, H, Nq, Nkv,
-                                  scale, stream);
+    return launch_fp8<128, 4, 0>(q8, k8, v8, descale, nullptr, nullptr, nullptr, o, lse, B, H,
+                                 Nq, Nkv, scale, stream);
+  return launch_fp8<64, 4, 0>(q8, k8, v8, descale, nullptr, nullptr, nullptr, o, lse, B, H, Nq,
+                              Nkv, scale, stream);
 }
 
 extern "C" int attn_fwd_fp8_rows(const void* q8, const void* k8, const void* v8,
@@ -355,8 +445,28 @@ extern "C" int attn_fwd_fp8_rows(const void* q8, const void* k8, const void* v8,
       (lse && !al(lse, 4)))
     return DTA_EALIGN;
   if (D == 128)
-    return launch_fp8<128, 4, true>(q8, k8, v8, v_descale, q_e8m0, k_e8m0, o, lse, B, H, Nq,
-                                    Nkv, scale, stream);
-  return launch_fp8<64, 4, true>(q8, k8, v8, v_descale, q_e8m0, k_e8m0, o, lse, B, H, Nq, Nkv,
-                                 scale, stream);
+    return launch_fp8<128, 4, 1>(q8, k8, v8, v_descale, q_e8m0, k_e8m0, nullptr, o, lse, B, H,
+                                 Nq, Nkv, scale, stream);
+  return launch_fp8<64, 4, 1>(q8, k8, v8, v_descale, q_e8m0, k_e8m0, nullptr, o, lse, B, H, Nq,
+                              Nkv, scale, stream);
+}
+
+extern "C" int attn_fwd_fp8_rows_v(const void* q8, const void* k8, const void* v8,
+                                   const void* q_e8m0, const void* k_e8m0, const void* v_e8m0,
+                                   void* o, float* lse, int B, int H, int Nq, int Nkv, int D,
+                                   float scale, hipStream_t stream) {
+  if (!q8 || !k8 || !v8 || !q_e8m0 || !k_e8m0 || !v_e8m0 || !o) return DTA_EINVAL;
+  if (B < 1 || H < 1 || Nq < 1 || Nkv < 1) return DTA_EINVAL;
+  if (!(scale >= 0.f) || !__builtin_isfinite(scale)) return DTA_EINVAL;
+  if (D != 64 && D != 128) return DTA_EUNSUPPORTED;
+  auto al = [](const void* p, uintptr_t a) {
+    return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0;
+  };
+  if (!al(q8, 16) || !al(k8, 16) || !al(v8, 16) || !al(o, 16) || (lse && !al(lse, 4)))
+    return DTA_EALIGN;
+  if (D == 128)
+    return launch_fp8<128, 4, 2>(q8, k8, v8, nullptr, q_e8m0, k_e8m0, v_e8m0, o, lse, B, H, Nq,
+                                 Nkv, scale, stream);
+  return launch_fp8<64, 4, 2>(q8, k8, v8, nullptr, q_e8m0, k_e8m0, v_e8m0, o, lse, B, H, Nq,
+                              Nkv, scale, stream);
 }

@@ -279,6 +279,33 @@ int attn_fwd_fp8_rows(const void* q8, const void* k8, const void* v8,
                       const float* v_descale, void* o, float* lse, int B, int H,
                       int Nq, int Nkv, int D, float scale, hipStream_t stream);
 
+/*
+ * attn_fwd_fp8_rows_v -- the row-wise variant with per-token power-of-two
+ * scales for V as well, and per-block power-of-two scales for P
+ * (ParaAttention guide, section "fp8 quantization": row-wise scaling as the
+ * more accurate option).
+ *   q8, k8, v8: E4M3 codes [B,H,Nq|Nkv,D], e.g. fp8_quant_rows_pow2 with
+ *               row_len = D (device, 16-byte aligned);
+ *   q_e8m0, k_e8m0, v_e8m0: one E8M0 byte per token, [B,H,Nq] / [B,H,Nkv]
+ *               (device); the scale of a token is 2^(byte - 127);
+ *   o: bf16 [B,H,Nq,D] (16-byte aligned); lse: float32 [B,H,Nq], or NULL.
+ * Q and K scales act as in attn_fwd_fp8_rows. V's scale is folded into the
+ * probabilities, pv_j = p_j 2^(ev_j - 127), with p_j = exp(s_j - m) against
+ * the running row maximum; pv is quantised to E4M3 with one power-of-two scale
+ * 2^e per (query, block of 32 consecutive keys), e the smallest integer with
+ * max pv <= 448 * 2^e (clamped to [-126, 127]). That scale is the P.V MFMA's
+ * operand scale, which the fp8 MFMA applies per 32 consecutive k.
+ *     O_i = sum_j P^_ij V8_j / sum_j p_ij,  LSE_i = m_i + ln sum_j p_ij
+ * with P^ the dequantised pv and V8 V's E4M3 values. Inside one block, pv
+ * values more than E4M3's span (about 2^17) below the block's largest round
+ * to zero. Errors: DTA_EINVAL (a null pointer, a size < 1, a negative or
+ * non-finite scale), DTA_EUNSUPPORTED (D other than 64 or 128), DTA_EALIGN.
+ */
+int attn_fwd_fp8_rows_v(const void* q8, const void* k8, const void* v8,
+                        const void* q_e8m0, const void* k_e8m0, const void* v_e8m0,
+                        void* o, float* lse, int B, int H, int Nq, int Nkv, int D,
+                        float scale, hipStream_t stream);
+
 /* Bytes of the workspace residual_diff and fp8_quant_per_tensor need. */
 size_t dta_ws_bytes(void);
 

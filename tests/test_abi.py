@@ -118,6 +118,22 @@ def test_fp8_rows_validation():
     assert f(ODD, *ok[1:], 1, 1, 1, 1, 128, 0.1, None) == _lib.DTA_EALIGN
 
 
+def test_fp8_rows_v_validation():
+    lib = _lib.lib()
+    f = lib.attn_fwd_fp8_rows_v
+    ok = (GOOD,) * 8                                   # q8 k8 v8 q_e k_e v_e o lse
+    for i in range(7):                                 # every required pointer
+        args = list(ok)
+        args[i] = None
+        assert f(*args, 1, 1, 1, 1, 128, 0.1, None) == _lib.DTA_EINVAL
+    assert f(*ok, 1, 1, 1, 0, 128, 0.1, None) == _lib.DTA_EINVAL
+    assert f(*ok, 1, 1, 1, 1, 128, -1.0, None) == _lib.DTA_EINVAL
+    assert f(*ok, 1, 1, 1, 1, 128, float("nan"), None) == _lib.DTA_EINVAL
+    assert f(*ok, 1, 1, 1, 1, 96, 0.1, None) == _lib.DTA_EUNSUPPORTED
+    assert f(ODD, *ok[1:], 1, 1, 1, 1, 128, 0.1, None) == _lib.DTA_EALIGN
+    assert f(*ok[:6], ODD, ok[7], 1, 1, 1, 1, 128, 0.1, None) == _lib.DTA_EALIGN
+
+
 def test_layout_validation():
     lib = _lib.lib()
     I = ctypes.c_int

@@ -132,3 +132,133 @@ def test_outlier_tokens_row_wise_beats_per_tensor():
     err_t = rel_l2(to64(o_t)[:, :, keep], o_ref[:, :, keep])
     print("outlier token: rel-L2 row-wise %.3e, per-tensor %.3e" % (err_r, err_t))
     assert err_r <= FP8_REL_L2_VS_BF16 and err_t > 2 * err_r
+
+
+# ---- per-token V and per-block P scales: attn_fwd_fp8_rows_v ----
+
+def _rows_v_path(q, k, v):
+    q8, eq = dta.fp8_quant_rows_pow2(q)
+    k8, ek = dta.fp8_quant_rows_pow2(k)
+    v8, ev = dta.fp8_quant_rows_pow2(v)
+    return q8, k8, v8, eq, ek, ev
+
+
+def _check_v(o8, l8, q, k, v, q8, k8, v8, eq, ek, ev, scale, rows=None, what=""):
+    o_dq, l_dq = oracle.attention_fp8_rows_v(q8.cpu().numpy(), k8.cpu().numpy(), v8.cpu().numpy(),
+                                             eq.cpu().numpy(), ek.cpu().numpy(), ev.cpu().numpy(),
+                                             scale, rows=rows)
+    o_bf, _ = oracle.attention(q.cpu(), k.cpu(), v.cpu(), scale, rows=rows)
+    if rows is not None:
+        rt = torch.from_numpy(rows).to(o8.device)
+        o8, l8 = o8[:, :, rt], l8[:, :, rt]
+    o8, l8 = to64(o8), to64(l8)
+    assert np.isfinite(o8).all() and np.isfinite(l8).all()
+    mean_abs = np.abs(o8 - o_bf).mean()
+    r_bf, r_dq = rel_l2(o8, o_bf), rel_l2(o8, o_dq)
+    e_l = np.abs(l8 - l_dq).max()
+    msg = "%s: O mean-abs %.3e, rel-L2 %.3e (bf16) %.3e (dequant), LSE %.3e" % (
+        what, mean_abs, r_bf, r_dq, e_l)
+    print(msg)
+    assert mean_abs <= FP8_O_MEAN_ABS and r_bf <= FP8_REL_L2_VS_BF16, msg
+    assert r_dq <= FP8_REL_L2_VS_DEQUANT and e_l <= LSE_ABS, msg
+    return r_bf
+
+
+@pytest.mark.parametrize("B,H,Nq,Nkv,D", [(1, 2, 300, 300, 128), (1, 3, 200, 131, 64),
+                                          (1, 1, 64, 1, 128), (2, 1, 97, 640, 128),
+                                          (1, 2, 129, 65, 64)])
+def test_attention_rows_v_shapes(B, H, Nq, Nkv, D):
+    print("CASE fp8 rows_v shape", B, H, Nq, Nkv, D, flush=True)
+    q, k, v = workloads.make_qkv(27, B, H, Nq, Nkv, D, device=DEV)
+    q8, k8, v8, eq, ek, ev = _rows_v_path(q, k, v)
+    o8, l8 = dta.attn_fwd_fp8_rows_v(q8, k8, v8, eq, ek, ev, D ** -0.5)
+    torch.cuda.synchronize()
+    _check_v(o8, l8, q, k, v, q8, k8, v8, eq, ek, ev, D ** -0.5, what="fp8 rows_v")
+
+
+def test_attention_rows_v_flux_sampled():
+    c = workloads.CONFIGS["flux_1024_fp8"]
+    print("CASE fp8 rows_v flux", flush=True)
+    q, k, v = workloads.workload_qkv("flux_1024_fp8", device=DEV)
+    q8, k8, v8, eq, ek, ev = _rows_v_path(q, k, v)
+    o8, l8 = dta.attn_fwd_fp8_rows_v(q8, k8, v8, eq, ek, ev, c["D"] ** -0.5)
+    torch.cuda.synchronize()
+    rows = workloads.sample_rows(c["config"], c["N"], 256, c["n_text"])
+    _check_v(o8, l8, q, k, v, q8, k8, v8, eq, ek, ev, c["D"] ** -0.5, rows=rows,
+             what="fp8 rows_v flux")
+
+
+def test_rows_v_uniform_scores_give_the_mean_of_v():
+    """Q = 0: every p is 1 and every block's pv is a power of two that E4M3
+    holds exactly, so O is the mean of the dequantised V rows (to float32
+    accumulation and one bf16 rounding) and LSE = ln N."""
+    B, H, N, D = 1, 2, 333, 128
+    print("CASE fp8 rows_v uniform scores", flush=True)
+    _, k, v = workloads.make_qkv(28, B, H, N, N, D, device=DEV)
+    g = torch.Generator().manual_seed(5)
+    v = (v.float() * torch.exp2(torch.randint(-6, 7, (B, H, N, 1), generator=g).float().to(DEV))
+         ).to(torch.bfloat16)
+    q = torch.zeros(B, H, N, D, dtype=torch.bfloat16, device=DEV)
+    q8, k8, v8, eq, ek, ev = _rows_v_path(q, k, v)
+    o8, l8 = dta.attn_fwd_fp8_rows_v(q8, k8, v8, eq, ek, ev, D ** -0.5)
+    torch.cuda.synchronize()
+    v_deq = oracle.e4m3_decode(v8.cpu().numpy()) * np.exp2(
+        ev.cpu().numpy().reshape(B, H, N, 1).astype(np.float64) - 127)
+    mean = np.broadcast_to(v_deq.mean(axis=2, keepdims=True), (B, H, N, D))
+    o = to64(o8)
+    ulp = np.maximum(np.abs(mean), 2.0 ** -126) * 2.0 ** -8
+    assert (np.abs(o - mean) <= ulp + 1e-5 * np.abs(v_deq).max()).all()
+    assert np.abs(to64(l8) - np.log(N)).max() < 1e-5
+
+
+def test_rows_v_outlier_value_token_beats_per_tensor_v():
+    B, H, N, D = 1, 2, 256, 128
+    print("CASE fp8 rows_v outlier V token", flush=True)
+    q, k, v = workloads.make_qkv(29, B, H, N, N, D, device=DEV)
+    v = v.float()
+    v[:, :, 7, :8] *= 65536.0
+    v[:, :, 7, 8:] = 0.0
+    v = v.to(torch.bfloat16)
+    scale = D ** -0.5
+    o_ref, _ = oracle.attention(q.cpu(), k.cpu(), v.cpu(), scale)
+    q8, k8, v8, eq, ek, ev = _rows_v_path(q, k, v)
+    o_v, _ = dta.attn_fwd_fp8_rows_v(q8, k8, v8, eq, ek, ev, scale)
+    vt, sv = dta.fp8_quant_per_tensor(v)
+    o_t, _ = dta.attn_fwd_fp8_rows(q8, k8, vt, eq, ek, sv, scale)
+    torch.cuda.synchronize()
+    d = slice(8, None)
+    err_v = rel_l2(to64(o_v)[..., d], o_ref[..., d])
+    err_t = rel_l2(to64(o_t)[..., d], o_ref[..., d])
+    print("outlier V token: rel-L2 per-token V %.3e, per-tensor V %.3e" % (err_v, err_t))
+    assert err_v <= FP8_REL_L2_VS_BF16 and err_t > 1.6 * err_v
+
+
+def test_rows_v_keeps_a_diffuse_tail():
+    """One query over 60000 keys: a peak and a tail at p ~ 1e-6 per key. The
+    x108 P scaling of attn_fwd_fp8_rows rounds the tail to zero; the
+    per-block P scales keep it (reference: exact attention on the
+    dequantised inputs)."""
+    N, D = 60000, 64
+    print("CASE fp8 rows_v diffuse tail", flush=True)
+    g = torch.Generator().manual_seed(30)
+    q = torch.zeros(1, 1, 1, D)
+    q[..., 0] = 4.0
+    k = torch.zeros(1, 1, N, D)
+    k[0, 0, 1:, 0] = -torch.log(torch.tensor(1e6)) / 4.0 * (1.0 + 0.01 * torch.randn(N - 1, generator=g))
+    v = 1.0 + torch.rand(1, 1, N, D, generator=g)
+    v[0, 0, 0] = 0.0
+    q, k, v = (t.to(torch.bfloat16).to(DEV) for t in (q, k, v))
+    q8, k8, v8, eq, ek, ev = _rows_v_path(q, k, v)
+    o_v, l_v = dta.attn_fwd_fp8_rows_v(q8, k8, v8, eq, ek, ev, 1.0)
+    vt, sv = dta.fp8_quant_per_tensor(v)
+    o_t, _ = dta.attn_fwd_fp8_rows(q8, k8, vt, eq, ek, sv, 1.0)
+    torch.cuda.synchronize()
+    deq = [oracle.e4m3_decode(c.cpu().numpy()) *
+           np.exp2(e.cpu().numpy().reshape(sh + (1,)).astype(np.float64) - 127)
+           for c, e, sh in ((q8, eq, (1, 1, 1)), (k8, ek, (1, 1, N)), (v8, ev, (1, 1, N)))]
+    o_ref, l_ref = oracle.attention(*deq, 1.0)
+    err_v = rel_l2(to64(o_v), o_ref)
+    err_t = rel_l2(to64(o_t), o_ref)
+    print("diffuse tail: rel-L2 per-block P %.3e, x108 P %.3e" % (err_v, err_t))
+    assert err_v < 0.02 and err_t > 0.9
+    assert np.abs(to64(l_v) - l_ref).max() < LSE_ABS
