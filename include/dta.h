@@ -298,9 +298,9 @@ int attn_fwd_fp8_rows(const void* q8, const void* k8, const void* v8,
  *     O_i = sum_j P^_ij V8_j / sum_j p_ij,  LSE_i = m_i + ln sum_j p_ij
  * with P^ the dequantised pv and V8 V's E4M3 values. Inside one block, pv
  * values more than E4M3's span (about 2^17) below the block's largest round
- * to zero. V exponent bytes must be <= 247 (p reaches 2^2 against the
+ * to zero. V exponent bytes must be <= 252 (p reaches 2^2 against the
  * running maximum, and pv must stay a finite float32); exponents of any
- * bf16 or float32 tensor are. Errors: DTA_EINVAL (a null pointer, a size < 1, a negative or
+ * bf16 or float32 tensor are (<= 247). Errors: DTA_EINVAL (a null pointer, a size < 1, a negative or
  * non-finite scale), DTA_EUNSUPPORTED (D other than 64 or 128), DTA_EALIGN.
  */
 int attn_fwd_fp8_rows_v(const void* q8, const void* k8, const void* v8,
