@@ -11,10 +11,17 @@
 //   LSE_i = m_i + ln l_i
 //
 // Same structure as the bf16 kernel: S^T = K . Q^T with one query per lane,
-// O^T += V^T . P^T, double-buffered padded K/V tiles in LDS fed by buffer
-// loads whose range check zero-fills rows past Nkv, a peeled masked tail
-// tile, a reference max raised only when a row outgrows it, XCD-aware tile
-// order.
+// O^T += V^T . P^T, padded K/V tiles in LDS fed by buffer loads whose range
+// check zero-fills rows past Nkv, a peeled masked tail tile, a reference max
+// raised only when a row outgrows it, XCD-aware tile order.
+// * At D = 128 with per-tensor or per-token Q/K scales a workgroup is 8 waves
+//   (two per SIMD) and the waves of the second half run skewed: each tile
+//   they first finish the previous tile's P.V, then score the current one, so
+//   the softmax of one wave of a SIMD falls under the other's MFMAs instead of
+//   beside them (the fp8 MFMA leaves about as much VALU work as MFMA work per
+//   tile). P.V one tile late needs that tile's V for one more barrier
+//   interval: three LDS buffers, still one barrier per tile. The other
+//   instances are 4 waves with two buffers.
 // The MFMA is v_mfma_f32_32x32x64_f8f6f4 with both operands E4M3: one
 // instruction contracts 64 values, so a 64-key tile takes one P.V MFMA per 32
 // head dims.
@@ -92,7 +99,7 @@ __device__ __forceinline__ i32x8 cat8(u32x4 lo, u32x4 hi) {
 // reduced over the lane pair (l, l ^ 32) and lane half g supplies block g's
 // scale to the P.V MFMA.
 template <int D, int NW, int MODE>
-__global__ __launch_bounds__(NW * 64, 2) void attn_fwd_fp8_kernel(
+__global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_fp8_kernel(
     const uint8_t* __restrict__ q, const uint8_t* __restrict__ k,
     const uint8_t* __restrict__ v, const float* __restrict__ descale,
     const uint8_t* __restrict__ q_e8, const uint8_t* __restrict__ k_e8,
@@ -101,12 +108,15 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_fp8_kernel(
   constexpr bool ROWS = MODE >= 1;
   using C = Fp8Cfg<D, NW>;
   constexpr int BN = C::kBN;
-  __shared__ __attribute__((aligned(16))) uint8_t ks[2][BN * C::kKS];
-  __shared__ __attribute__((aligned(16))) uint8_t vs[2][BN * C::kVS];
-  __shared__ __attribute__((aligned(16))) uint8_t ves[2][MODE == 2 ? BN : 4];   // V exponents
+  constexpr bool SKEW = NW == 8;
+  constexpr int NBUF = SKEW ? 3 : 2;
+  __shared__ __attribute__((aligned(16))) uint8_t ks[NBUF][BN * C::kKS];
+  __shared__ __attribute__((aligned(16))) uint8_t vs[NBUF][BN * C::kVS];
+  __shared__ __attribute__((aligned(16))) uint8_t ves[NBUF][MODE == 2 ? BN : 4];   // V exponents
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
+  const bool late = SKEW && __builtin_amdgcn_readfirstlane(wave) >= NW / 2;
   const int g = lane >> 5, l32 = lane & 31;
   const int blk = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = blk / n_qt, qt = blk - bh * n_qt;
@@ -198,15 +208,11 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_fp8_kernel(
   store_tile(0);
   __syncthreads();
 
-  auto tile = [&](int j, auto buf_tag, auto mask_tag) {
+  // S^T of tile j (K in kt, V exponents in vte_buf for MODE 2) and its
+  // softmax into the P operand pb and its scale sb_e.
+  auto qk_softmax = [&](int j, const uint8_t* kt, const uint8_t* vte_buf, const int (&sk_e)[2],
+                        i32x8& pb, int& sb_e, auto mask_tag) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
-    constexpr int buf = decltype(buf_tag)::value;
-    const bool has_next = j + 1 < n_tiles;
-    const int sk_e[2] = {sk_next[0], sk_next[1]};
-    if (has_next) load_tile(j + 1);
-    const uint8_t* kt = ks[buf];
-    const uint8_t* vt = vs[buf];
-
     f32x16 s[2] = {f32x16{}, f32x16{}};
 #pragma unroll
     for (int kk = 0; kk < D / 64; ++kk)
@@ -243,8 +249,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_fp8_kernel(
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
     }
-    i32x8 pb;
-    int sb_e = 127;                      // P.V MFMA B operand scale (E8M0)
+    sb_e = 127;
     if constexpr (MODE != 2) {
       const float m448 = m_run - kLog2PScale;
       float rs = 0.f;
@@ -262,7 +267,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_fp8_kernel(
             }
             rs += p[u];
           }
-          int wd = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+          // The first conversion writes the low half; the high half of `old`
+          // (any dead register, here p[0]'s) is overwritten by the second.
+          int wd = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], __float_as_int(p[0]), false);
           wd = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], wd, true);
           pb[kb * 4 + w] = wd;
           asm volatile("" : "+v"(rs));
@@ -272,7 +279,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_fp8_kernel(
       // p = 2^(s c - m_run) in (0, 2^kTau8]; l_run sums p. pv = p 2^(ev-127)
       // for this lane's keys kb*32 + 8w + 4g + u (4 consecutive exponent
       // bytes per (kb, w): one aligned LDS word).
-      const uint8_t* vte = ves[buf];
+      const uint8_t* vte = vte_buf;
       float pv[2][16];
       float rs = 0.f, bmax[2] = {0.f, 0.f};
 #pragma unroll
@@ -326,7 +333,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_fp8_kernel(
           pb[kb * 4 + w] = __builtin_bit_cast(int, wd);
         }
     }
-
+  };
+  // O^T += V^T . P^T for the tile whose V is in vt.
+  auto pv = [&](const uint8_t* vt, const i32x8& pb, int sb_e) __attribute__((always_inline)) {
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
       i32x2 part[4];
@@ -343,26 +352,84 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_fp8_kernel(
         oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, pb, oacc[db], 0, 0, 0, 0,
                                                                     0, 0);
     }
-
-    if (has_next) store_tile(buf ^ 1);
+  };
+  i32x8 pb_late = {};
+  int sb_late = 127;
+  // One K/V tile in buffer buf = j % NBUF; MASK only for a ragged last tile.
+  // The late waves (the second wave of every SIMD) finish tile j-1 first (its
+  // P is in pb_late, its V still in buffer (j-1) % NBUF), then score tile j;
+  // their last P.V follows the loop. The tile staged during tile j goes to
+  // buffer (j+1) % NBUF, which no wave reads in this barrier interval.
+  auto tile = [&](int j, auto buf_tag, auto mask_tag,
+                  auto late_tag) __attribute__((always_inline)) {
+    constexpr int buf = decltype(buf_tag)::value;
+    constexpr bool LATE = decltype(late_tag)::value;
+    constexpr int pbuf = (buf + NBUF - 1) % NBUF;
+    const bool has_next = j + 1 < n_tiles;
+    const int sk_e[2] = {sk_next[0], sk_next[1]};
+    if (has_next) load_tile(j + 1);
+    if constexpr (LATE) {
+      if (j > 0) pv(vs[pbuf], pb_late, sb_late);
+      qk_softmax(j, ks[buf], ves[buf], sk_e, pb_late, sb_late, mask_tag);
+    } else {
+      i32x8 pb;
+      int sb_e;
+      qk_softmax(j, ks[buf], ves[buf], sk_e, pb, sb_e, mask_tag);
+      pv(vs[buf], pb, sb_e);
+    }
+    if (has_next) store_tile((buf + 1) % NBUF);
     __syncthreads();
   };
 
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
+  using B2 = std::integral_constant<int, 2>;
   const int n_full = (Nkv % BN == 0) ? n_tiles : n_tiles - 1;
-  int j = 0;
-  for (; j + 1 < n_full; j += 2) {
-    tile(j, B0{}, std::false_type{});
-    tile(j + 1, B1{}, std::false_type{});
-  }
-  if (j < n_full) tile(j++, B0{}, std::false_type{});
-  if (j < n_tiles) {
-    if (j & 1)
-      tile(j, B1{}, std::true_type{});
-    else
-      tile(j, B0{}, std::true_type{});
-  }
+  auto run = [&](auto late_tag) __attribute__((always_inline)) {
+    constexpr bool LATE = decltype(late_tag)::value;
+    int j = 0;
+    if constexpr (NBUF == 3) {
+      for (; j + 2 < n_full; j += 3) {
+        tile(j, B0{}, std::false_type{}, late_tag);
+        tile(j + 1, B1{}, std::false_type{}, late_tag);
+        tile(j + 2, B2{}, std::false_type{}, late_tag);
+      }
+      for (; j < n_full; ++j) {
+        if (j % 3 == 0)
+          tile(j, B0{}, std::false_type{}, late_tag);
+        else
+          tile(j, B1{}, std::false_type{}, late_tag);
+      }
+      if (j < n_tiles) {
+        if (j % 3 == 0)
+          tile(j, B0{}, std::true_type{}, late_tag);
+        else if (j % 3 == 1)
+          tile(j, B1{}, std::true_type{}, late_tag);
+        else
+          tile(j, B2{}, std::true_type{}, late_tag);
+      }
+      if constexpr (LATE) {
+        const int lb = (n_tiles - 1) % 3;
+        pv(vs[lb], pb_late, sb_late);
+      }
+    } else {
+      for (; j + 1 < n_full; j += 2) {
+        tile(j, B0{}, std::false_type{}, late_tag);
+        tile(j + 1, B1{}, std::false_type{}, late_tag);
+      }
+      if (j < n_full) tile(j++, B0{}, std::false_type{}, late_tag);
+      if (j < n_tiles) {
+        if (j & 1)
+          tile(j, B1{}, std::true_type{}, late_tag);
+        else
+          tile(j, B0{}, std::true_type{}, late_tag);
+      }
+    }
+  };
+  if (late)
+    run(std::true_type{});
+  else
+    run(std::false_type{});
 
   // MODE 0/1: l_run holds 108 l and O = s_v * acc / (108 l). MODE 2: l_run
   // holds l and O = acc / l (V's scale is in P).
@@ -424,7 +491,7 @@ extern "C" int attn_fwd_fp8(const void* q8, const void* k8, const void* v8,
       (lse && !al(lse, 4)))
     return DTA_EALIGN;
   if (D == 128)
-    return launch_fp8<128, 4, 0>(q8, k8, v8, descale, nullptr, nullptr, nullptr, o, lse, B, H,
+    return launch_fp8<128, 8, 0>(q8, k8, v8, descale, nullptr, nullptr, nullptr, o, lse, B, H,
                                  Nq, Nkv, scale, stream);
   return launch_fp8<64, 4, 0>(q8, k8, v8, descale, nullptr, nullptr, nullptr, o, lse, B, H, Nq,
                               Nkv, scale, stream);
@@ -445,7 +512,7 @@ extern "C" int attn_fwd_fp8_rows(const void* q8, const void* k8, const void* v8,
       (lse && !al(lse, 4)))
     return DTA_EALIGN;
   if (D == 128)
-    return launch_fp8<128, 4, 1>(q8, k8, v8, v_descale, q_e8m0, k_e8m0, nullptr, o, lse, B, H,
+    return launch_fp8<128, 8, 1>(q8, k8, v8, v_descale, q_e8m0, k_e8m0, nullptr, o, lse, B, H,
                                  Nq, Nkv, scale, stream);
   return launch_fp8<64, 4, 1>(q8, k8, v8, v_descale, q_e8m0, k_e8m0, nullptr, o, lse, B, H, Nq,
                               Nkv, scale, stream);

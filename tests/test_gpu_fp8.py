@@ -76,3 +76,34 @@ def test_fp8_flux_1024_sampled_rows():
     torch.cuda.synchronize()
     rows = workloads.sample_rows(c["config"], c["N"], 256, c["n_text"])
     _check(o8, l8, q, k, v, q8, k8, v8, ds, c["D"] ** -0.5, rows=rows, what="fp8 flux")
+
+
+@pytest.mark.parametrize("Nkv", [1, 40, 64, 65, 128, 150, 192, 256, 300, 320, 385])
+def test_fp8_attention_tile_counts(Nkv):
+    """K/V lengths of 1 to 7 tiles of 64 keys, full and ragged last tile: the
+    8-wave D = 128 kernel rotates three LDS buffers and its skewed waves finish
+    the last tile's P.V after the loop, so every residue of the tile count
+    mod 3 and both tail kinds are covered."""
+    print("CASE fp8 tile count", Nkv, flush=True)
+    q, k, v = workloads.make_qkv(29, 1, 2, 300, Nkv, 128, device=DEV)
+    q8, k8, v8, ds = _quant3(q, k, v)
+    o8, l8 = dta.attn_fwd_fp8(q8, k8, v8, ds, 128 ** -0.5)
+    torch.cuda.synchronize()
+    _check(o8, l8, q, k, v, q8, k8, v8, ds, 128 ** -0.5, what="fp8 Nkv=%d" % Nkv)
+
+
+@pytest.mark.parametrize("Nkv", [300, 1024])
+def test_fp8_query_position_invariance(Nkv):
+    """A query's O and LSE do not depend on which wave computes it. Rolling
+    the queries by 128 rows moves every query between the first and the
+    second half of a 256-query workgroup (the on-time and the skewed waves);
+    O and LSE must roll bit for bit."""
+    print("CASE fp8 query roll", Nkv, flush=True)
+    q, k, v = workloads.make_qkv(31, 1, 2, 512, Nkv, 128, device=DEV)
+    q8, k8, v8, ds = _quant3(q, k, v)
+    o_a, l_a = dta.attn_fwd_fp8(q8, k8, v8, ds, 128 ** -0.5)
+    o_b, l_b = dta.attn_fwd_fp8(torch.roll(q8, 128, dims=2).contiguous(), k8, v8, ds,
+                                128 ** -0.5)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.roll(o_a, 128, dims=2), o_b)
+    assert torch.equal(torch.roll(l_a, 128, dims=2), l_b)

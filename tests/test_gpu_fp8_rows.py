@@ -262,3 +262,32 @@ def test_rows_v_keeps_a_diffuse_tail():
     print("diffuse tail: rel-L2 per-block P %.3e, x108 P %.3e" % (err_v, err_t))
     assert err_v < 0.02 and err_t > 0.9
     assert np.abs(to64(l_v) - l_ref).max() < LSE_ABS
+
+
+@pytest.mark.parametrize("Nkv", [40, 128, 150, 192, 385])
+def test_attention_rows_tile_counts(Nkv):
+    """Tile counts 1 to 7 with full and ragged last tiles for the skewed
+    8-wave instance (three LDS buffers, the skewed waves' last P.V after the
+    loop)."""
+    print("CASE fp8 rows tile count", Nkv, flush=True)
+    q, k, v = workloads.make_qkv(29, 1, 2, 300, Nkv, 128, device=DEV)
+    q8, k8, v8, eq, ek, sv = _rows_path(q, k, v)
+    o8, l8 = dta.attn_fwd_fp8_rows(q8, k8, v8, eq, ek, sv, 128 ** -0.5)
+    torch.cuda.synchronize()
+    _check(o8, l8, q, k, v, q8, k8, v8, eq, ek, sv, 128 ** -0.5, what="rows Nkv=%d" % Nkv)
+
+
+def test_rows_query_position_invariance():
+    """Rolling the queries (and their exponents) by 128 rows moves them between
+    the on-time and the skewed waves of a workgroup; O and LSE roll bit for
+    bit."""
+    print("CASE fp8 rows query roll", flush=True)
+    q, k, v = workloads.make_qkv(31, 1, 2, 512, 300, 128, device=DEV)
+    q8, k8, v8, eq, ek, sv = _rows_path(q, k, v)
+    o_a, l_a = dta.attn_fwd_fp8_rows(q8, k8, v8, eq, ek, sv, 128 ** -0.5)
+    o_b, l_b = dta.attn_fwd_fp8_rows(torch.roll(q8, 128, dims=2).contiguous(), k8, v8,
+                                     torch.roll(eq, 128, dims=2).contiguous(), ek, sv,
+                                     128 ** -0.5)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.roll(o_a, 128, dims=2), o_b)
+    assert torch.equal(torch.roll(l_a, 128, dims=2), l_b)
