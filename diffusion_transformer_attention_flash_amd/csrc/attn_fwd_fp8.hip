@@ -112,7 +112,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_fp8_kernel(
   constexpr int NBUF = SKEW ? 3 : 2;
   __shared__ __attribute__((aligned(16))) uint8_t ks[NBUF][BN * C::kKS];
   __shared__ __attribute__((aligned(16))) uint8_t vs[NBUF][BN * C::kVS];
-  __shared__ __attribute__((aligned(16))) uint8_t ves[NBUF][MODE == 2 ? BN : 4];   // V exponents
+  // MODE 2: the V scales 2^(e - 127) of the tile's keys, as floats.
+  __shared__ __attribute__((aligned(16))) float ves[NBUF][MODE == 2 ? BN : 4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -188,7 +189,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_fp8_kernel(
       *reinterpret_cast<u32x4*>(&vs[buf][v8_row(r) * C::kVS + st_c * 16]) = vreg[it];
     }
     if constexpr (MODE == 2) {
-      if (tid < BN) ves[buf][tid] = (uint8_t)ve_next;
+      if (tid < BN) ves[buf][tid] = __builtin_amdgcn_ldexpf(1.0f, ve_next - 127);
     }
   };
 
@@ -208,9 +209,9 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_fp8_kernel(
   store_tile(0);
   __syncthreads();
 
-  // S^T of tile j (K in kt, V exponents in vte_buf for MODE 2) and its
+  // S^T of tile j (K in kt, V scales in vte_buf for MODE 2) and its
   // softmax into the P operand pb and its scale sb_e.
-  auto qk_softmax = [&](int j, const uint8_t* kt, const uint8_t* vte_buf, const int (&sk_e)[2],
+  auto qk_softmax = [&](int j, const uint8_t* kt, const float* vte_buf, const int (&sk_e)[2],
                         i32x8& pb, int& sb_e, auto mask_tag) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
     f32x16 s[2] = {f32x16{}, f32x16{}};
@@ -277,16 +278,16 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_fp8_kernel(
       l_run += rs;
     } else {
       // p = 2^(s c - m_run) in (0, 2^kTau8]; l_run sums p. pv = p 2^(ev-127)
-      // for this lane's keys kb*32 + 8w + 4g + u (4 consecutive exponent
-      // bytes per (kb, w): one aligned LDS word).
-      const uint8_t* vte = vte_buf;
+      // for this lane's keys kb*32 + 8w + 4g + u (4 consecutive V scales per
+      // (kb, w): one aligned 16-byte LDS read).
+      const float* vte = vte_buf;
       float pv[2][16];
       float rs = 0.f, bmax[2] = {0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          const uint32_t ew = *reinterpret_cast<const uint32_t*>(vte + kb * 32 + 8 * w + 4 * g);
+          const f32x4 ev = *reinterpret_cast<const f32x4*>(vte + kb * 32 + 8 * w + 4 * g);
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
             const int r = 4 * w + u;
@@ -295,8 +296,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_fp8_kernel(
               if (kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3) >= key_lim) p = 0.f;
             }
             rs += p;
-            const int ev = (int)((ew >> (8 * u)) & 0xFFu) - 127;
-            pv[kb][r] = __builtin_amdgcn_ldexpf(p, ev);
+            pv[kb][r] = p * ev[u];        // exact: a power-of-two factor
             bmax[kb] = fmaxf(bmax[kb], pv[kb][r]);
           }
           asm volatile("" : "+v"(rs));
