@@ -114,6 +114,10 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_fp8_kernel(
   __shared__ __attribute__((aligned(16))) uint8_t vs[NBUF][BN * C::kVS];
   // MODE 2: the V scales 2^(e - 127) of the tile's keys, as floats.
   __shared__ __attribute__((aligned(16))) float ves[NBUF][MODE == 2 ? BN : 4];
+  // Epilogue staging of O (the 8-wave instances): 32 rows of 272 bytes per
+  // wave. (The 4-wave rows_v instance keeps direct stores: two workgroups
+  // share a CU there, and its video-shape time rose 0.7% with the staging.)
+  __shared__ __attribute__((aligned(16))) uint8_t ostg[NW == 8 ? NW * 32 * 272 : 16];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -435,7 +439,37 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_fp8_kernel(
   // holds l and O = acc / l (V's scale is in P).
   const float lt = xhalf_sum8(l_run);
   const float f = s_v / lt;
-  if (row < Nq) {
+  if constexpr (D == 128 && NW == 8) {
+    // O goes through LDS so that each global store covers whole 256-byte
+    // rows (16 lanes per row) instead of 16 bytes of each of 32 rows. Each
+    // wave stages its 32 rows (272-byte pitch) in its own slice and reads
+    // back only that slice: no barrier. Every lane takes part, since the rows
+    // a lane stores are not its own; the indices derive from `row` and `g`.
+    constexpr int kPitch = 272, kSlice = 32 * kPitch;
+    const int r_lo = row & 31, wv = (row >> 5) & (NW - 1);
+    uint8_t* stg = ostg + wv * kSlice;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const f32x16& a = oacc[db];
+        u32x2 w = {pack_bf16x2(a[4 * jj] * f, a[4 * jj + 1] * f),
+                   pack_bf16x2(a[4 * jj + 2] * f, a[4 * jj + 3] * f)};
+        *reinterpret_cast<u32x2*>(stg + r_lo * kPitch + (db * 32 + 8 * jj + 4 * g) * 2) = w;
+      }
+    if (g == 0 && lse != nullptr && row < Nq)
+      lse[(int64_t)bh * Nq + row] =
+          (m_run + log2f(lt) - (MODE == 2 ? 0.0f : kLog2PScale)) * kLn2;
+    // Store kk covers rows 4kk .. 4kk+3 of the wave; lane = 16 * (row % 4) + chunk.
+    const int row0 = row - r_lo, sub = 2 * g + (r_lo >> 4), ch = r_lo & 15;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const int r = 4 * kk + sub;
+      const u32x4 val = *reinterpret_cast<const u32x4*>(stg + r * kPitch + ch * 16);
+      if (row0 + r < Nq)
+        *reinterpret_cast<u32x4*>(o + q_base + (int64_t)(row0 + r) * D + ch * 8) = val;
+    }
+  } else if (row < Nq) {
     uint16_t* orow = o + q_base + (int64_t)row * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
