@@ -268,33 +268,76 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_bf16_kernel(
   // Epilogue: lane owns query `row` and dims db*32 + 8*(r/4) + 4g + r%4.
   const float lt = xhalf_sum(l_run);
   const int64_t li = (int64_t)bh * Nq + row;
-  if constexpr (!ACCUM && D == 128 && NW == 8) {
-    // O goes through LDS so that the global stores are whole 256-byte rows
-    // (16 lanes per row) instead of 16 bytes of each of 32 rows per store.
-    // The last tile's barrier has retired every K/V read; each wave stages
-    // its 32 rows (272-byte pitch, conflict-free 8-byte writes) in its own
-    // slice of the K or V buffers and reads back only its own slice, so no
-    // further barrier is needed. Every lane takes part: the rows a lane
-    // stores are not its own. The indices derive from `row` and `g` alone,
-    // which keeps the loop's register allocation as without this epilogue.
+  if constexpr (D == 128 && NW == 8) {
+    // O goes through LDS so that the global loads and stores of O are whole
+    // 256-byte rows (16 lanes per row) instead of 16 bytes of each of 32
+    // rows per instruction. The last tile's barrier has retired every K/V
+    // read; each wave uses its own slice of the K/V buffers (32 rows at a
+    // 272-byte pitch, conflict-free 8-byte accesses) and touches no other
+    // slice, so no further barrier is needed. Every lane takes part: the rows
+    // a lane loads and stores are not its own. The indices derive from `row`
+    // and `g` alone, which keeps the loop's register allocation as without
+    // this epilogue.
     constexpr int kPitch = 272, kSlice = 32 * kPitch;
     static_assert(sizeof(ks) >= 4 * kSlice && sizeof(vs) >= 4 * kSlice, "O staging");
-    const float inv = 1.0f / lt;
     const int r_lo = row & 31, wv = (row >> 5) & 7;
     uint8_t* stg = wv < 4 ? reinterpret_cast<uint8_t*>(&ks[0][0]) + wv * kSlice
                           : reinterpret_cast<uint8_t*>(&vs[0][0]) + (wv - 4) * kSlice;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const f32x16& a = oacc[db];
-        u32x2 w = {pack_bf16x2(a[4 * jj] * inv, a[4 * jj + 1] * inv),
-                   pack_bf16x2(a[4 * jj + 2] * inv, a[4 * jj + 3] * inv)};
-        *reinterpret_cast<u32x2*>(stg + r_lo * kPitch + (db * 32 + 8 * jj + 4 * g) * 2) = w;
-      }
-    if (g == 0 && lse != nullptr && row < Nq) lse[li] = (m_run + log2f(lt)) * kLn2;
-    // Store kk covers rows 4kk .. 4kk+3 of the wave; lane = 16 * (row % 4) + chunk.
+    // Coalesced access kk covers rows 4kk .. 4kk+3 of the wave; lane =
+    // 16 * (row % 4) + 16-byte chunk.
     const int row0 = row - r_lo, sub = 2 * g + (r_lo >> 4), ch = r_lo & 15;
+    if constexpr (!ACCUM) {
+      const float inv = 1.0f / lt;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const f32x16& a = oacc[db];
+          u32x2 w = {pack_bf16x2(a[4 * jj] * inv, a[4 * jj + 1] * inv),
+                     pack_bf16x2(a[4 * jj + 2] * inv, a[4 * jj + 3] * inv)};
+          *reinterpret_cast<u32x2*>(stg + r_lo * kPitch + (db * 32 + 8 * jj + 4 * g) * 2) = w;
+        }
+      if (g == 0 && lse != nullptr && row < Nq) lse[li] = (m_run + log2f(lt)) * kLn2;
+    } else {
+      // The running O rows into the slice, then the two-part merge below in
+      // place there (rows past Nq hold zeros and are never stored).
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        const int r = 4 * kk + sub;
+        u32x4 val = {0u, 0u, 0u, 0u};
+        if (row0 + r < Nq)
+          val = *reinterpret_cast<const u32x4*>(o + q_base + (int64_t)(row0 + r) * D + ch * 8);
+        *reinterpret_cast<u32x4*>(stg + r * kPitch + ch * 16) = val;
+      }
+      // Two-part log-sum-exp merge in the log2 domain, as below.
+      const float lc = m_run + log2f(lt);
+      const float lr = row < Nq ? lse[li] * kLog2e : -INFINITY;
+      const float mm = fmaxf(lc, lr);
+      const float wr = __builtin_amdgcn_exp2f(lr - mm);
+      const float wc = __builtin_amdgcn_exp2f(lc - mm);
+      const float den = wr + wc;
+      const float ar = wr / den;
+      const float ac = wc / (den * lt);
+      const bool use_r = wr > 0.f;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          uint8_t* cell = stg + r_lo * kPitch + (db * 32 + 8 * jj + 4 * g) * 2;
+          const u32x2 prev = *reinterpret_cast<const u32x2*>(cell);
+          const f32x16& a = oacc[db];
+          float x[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t wv2 = prev[e >> 1];
+            const float orv = bf16_bits_to_f32((e & 1) ? (wv2 >> 16) : (wv2 & 0xFFFF));
+            x[e] = a[4 * jj + e] * ac + (use_r ? orv * ar : 0.f);
+          }
+          *reinterpret_cast<u32x2*>(cell) =
+              u32x2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+        }
+      if (g == 0 && row < Nq) lse[li] = (mm + log2f(den)) * kLn2;
+    }
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
       const int r = 4 * kk + sub;
