@@ -186,8 +186,9 @@ int fbcache_step(const void* r, const void* r_prev, int64_t n, float threshold,
  * x8       uint8 [n], 16-byte aligned, written
  * descale  float, one device scalar, written with s
  * ws       as for residual_diff (may be the same buffer, not concurrently)
- * Enqueues three kernels: partial maxima, their one-workgroup finish into
- * descale, and the cast.
+ * Enqueues two kernels: partial maxima into ws, and the cast, every
+ * workgroup of which reduces the partials itself; workgroup 0 writes
+ * descale.
  */
 int fp8_quant_per_tensor(const void* x, int64_t n, void* x8, float* descale,
                          void* ws, hipStream_t stream);
