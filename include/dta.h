@@ -300,9 +300,10 @@ int attn_fwd_fp8_rows(const void* q8, const void* k8, const void* v8,
  * with P^ the dequantised pv and V8 V's E4M3 values. Inside one block, pv
  * values more than E4M3's span (about 2^17) below the block's largest round
  * to zero. V exponent bytes must be <= 252 (p reaches 2^2 against the
- * running maximum, and pv must stay a finite float32); exponents of any
- * bf16 or float32 tensor are (<= 247). Errors: DTA_EINVAL (a null pointer, a size < 1, a negative or
- * non-finite scale), DTA_EUNSUPPORTED (D other than 64 or 128), DTA_EALIGN.
+ * running maximum, and pv must stay a finite float32); the exponents of any
+ * bf16 or float32 tensor are (<= 247). Errors: DTA_EINVAL (a null pointer, a
+ * size < 1, a negative or non-finite scale), DTA_EUNSUPPORTED (D other than
+ * 64 or 128), DTA_EALIGN.
  */
 int attn_fwd_fp8_rows_v(const void* q8, const void* k8, const void* v8,
                         const void* q_e8m0, const void* k_e8m0, const void* v_e8m0,
