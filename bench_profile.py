@@ -13,6 +13,13 @@
             [--first-of-run] --out OUT.json --cmd "..."
         Per-launch HBM bytes of one kernel from FETCH_SIZE / WRITE_SIZE runs,
         each scaled by what the same counter reads for the copy above.
+    python bench_profile.py summarize-counters --dir DIR [--dir DIR ...]
+            --sel "LABEL|REGEX|GRID|PLACE" [--sel ...]
+            --out OUT.md --title "..." --cmd "..."
+        Median per dispatch of every counter found in the counter directories,
+        for each selection of kernels (name regex, grid size or *, and the
+        dispatch's place in a run of consecutive dispatches of one kernel:
+        first, later or any, optionally :N for runs of length N).
 """
 
 import argparse
@@ -168,6 +175,85 @@ def cmd_summarize_pmc(args):
     print(json.dumps(out, indent=1))
 
 
+def _counter_rows(d):
+    rows = []
+    for path in _find(d, "counter_collection.csv"):
+        with open(path) as f:
+            rows += list(csv.DictReader(f))
+    return rows
+
+
+def cmd_summarize_counters(args):
+    """Counter medians per kernel selection. A selection is
+    LABEL|REGEX|GRID|PLACE with GRID an integer or *, and PLACE first (the
+    dispatch opens a run of consecutive dispatches of its kernel), later or
+    any, with an optional :N that also requires the run to be N long."""
+    sels = []
+    for s in args.sel:
+        label, rx, grid, place = s.split("|")
+        sels.append((label, re.compile(rx), None if grid == "*" else int(grid), place))
+    table = {}          # (label, counter) -> [values]
+    counters = []
+    for d in args.dir:
+        rows = _counter_rows(d)
+        if not rows:
+            continue
+        did, kn = _col(rows[0], "dispatch", "id"), _col(rows[0], "kernel", "name")
+        cn, cv = _col(rows[0], "counter", "name"), _col(rows[0], "counter", "value")
+        gcol = None
+        try:
+            gcol = _col(rows[0], "grid", "size")
+        except KeyError:
+            pass
+        # One entry per dispatch: name, grid, counters.
+        disp = {}
+        for r in rows:
+            e = disp.setdefault(int(r[did]), {"name": r[kn], "grid": r.get(gcol), "c": {}})
+            e["c"][r[cn]] = e["c"].get(r[cn], 0.0) + float(r[cv])
+        # Runs of consecutive dispatches of one kernel: position and length.
+        order = sorted(disp)
+        runs, cur = [], []
+        for i in order:
+            if cur and disp[i]["name"] != disp[cur[-1]]["name"]:
+                runs.append(cur)
+                cur = []
+            cur.append(i)
+        if cur:
+            runs.append(cur)
+        for run in runs:
+            for pos, i in enumerate(run):
+                disp[i]["first"], disp[i]["run"] = pos == 0, len(run)
+        for i in order:
+            e = disp[i]
+            for label, rx, grid, place in sels:
+                if not rx.search(e["name"]):
+                    continue
+                if grid is not None and e["grid"] is not None and int(e["grid"]) != grid:
+                    continue
+                kind, _, n = place.partition(":")
+                if (kind == "first" and not e["first"]) or (kind == "later" and e["first"]):
+                    continue
+                if n and e["run"] != int(n):
+                    continue
+                for c, v in e["c"].items():
+                    if c not in counters:
+                        counters.append(c)
+                    table.setdefault((label, c), []).append(v)
+    lines = ["# rocprofv3 counters: %s" % args.title, "", "Command (repo root): `%s`" % args.cmd,
+             "", "Median per dispatch (dispatches counted in brackets).", "",
+             "| kernel | " + " | ".join(counters) + " |",
+             "|---|" + "---:|" * len(counters)]
+    for label, _, _, _ in sels:
+        cells = []
+        for c in counters:
+            v = table.get((label, c))
+            cells.append("%.4g (%d)" % (statistics.median(v), len(v)) if v else "-")
+        lines.append("| %s | %s |" % (label, " | ".join(cells)))
+    with open(args.out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd_name", required=True)
@@ -186,9 +272,16 @@ def main():
     p.add_argument("--first-of-run", action="store_true")
     p.add_argument("--copy-mib", type=int, default=1024)
     p.add_argument("--grid", type=int, default=None)
+    p = sub.add_parser("summarize-counters")
+    p.add_argument("--dir", action="append", required=True)
+    p.add_argument("--sel", action="append", required=True)
+    p.add_argument("--out", required=True)
+    p.add_argument("--title", default="")
+    p.add_argument("--cmd", required=True)
     args = ap.parse_args()
     {"copy": cmd_copy, "summarize-trace": cmd_summarize_trace,
-     "summarize-pmc": cmd_summarize_pmc}[args.cmd_name](args)
+     "summarize-pmc": cmd_summarize_pmc,
+     "summarize-counters": cmd_summarize_counters}[args.cmd_name](args)
 
 
 if __name__ == "__main__":
