@@ -21,7 +21,9 @@
 //   beside them (the fp8 MFMA leaves about as much VALU work as MFMA work per
 //   tile). P.V one tile late needs that tile's V for one more barrier
 //   interval: three LDS buffers, still one barrier per tile. The other
-//   instances are 4 waves with two buffers.
+//   instances are 4 waves with two buffers. The 8-wave instances also stage
+//   O through LDS in the epilogue, so that each global store covers whole
+//   output rows.
 // The MFMA is v_mfma_f32_32x32x64_f8f6f4 with both operands E4M3: one
 // instruction contracts 64 values, so a 64-key tile takes one P.V MFMA per 32
 // head dims.
