@@ -75,6 +75,31 @@ def test_peaked_rows(D):
     assert_bf16_attention(o, lse, o_ref, lse_ref, "peaked")
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_extreme_logits(D):
+    """Q x64 before rounding: the logits spread over hundreds of units, every
+    row's softmax is nearly one-hot, and the running max jumps between tiles
+    by far more than the lazy-rescale slack (the rescale factor underflows
+    to 0). The same attention as a fused ring over three chunks."""
+    _case("extreme logits", D=D)
+    q, k, v = workloads.make_qkv(13, 1, 2, 300, 1000, D, qknorm=True, device=DEV, q_gain=64.0)
+    # A nearly one-hot row returns one V row, up to ~4.4 here, where one bf16
+    # rounding alone is up to 1.6e-2; V / 4 (exact) keeps |O| near 1 so that
+    # the absolute O gate measures the kernel, not the output format.
+    v = v * 0.25
+    scale = D ** -0.5
+    o, lse = _run(q, k, v, scale)
+    o_ref, lse_ref = oracle.attention(q.cpu(), k.cpu(), v.cpu(), scale)
+    assert np.abs(lse_ref).max() > 50
+    assert_bf16_attention(o, lse, o_ref, lse_ref, "extreme")
+    chunks = workloads.split_kv(k, v, [333, 1, 666])
+    o_r, lse_r = dta.attn_fwd(q, chunks[0][0], chunks[0][1], scale)
+    for kc, vc in chunks[1:]:
+        dta.attn_fwd_accum(q, kc, vc, o_r, lse_r, scale)
+    torch.cuda.synchronize()
+    assert_bf16_attention(o_r, lse_r, o_ref, lse_ref, "extreme ring")
+
+
 def test_closed_forms_on_gpu():
     _case("closed-forms")
     D, n = 128, 333
