@@ -7,7 +7,8 @@ attention shape (B=1, H=24, N=4608 = 512 text + 4096 image tokens, D=128):
   1. attn_fwd, bf16, over the full K/V                       (O, LSE)
   2. the ring-step emulation: attn_fwd over 8 seeded uneven contiguous K/V
      chunks, then attn_merge of the 8 partials
-  3. the fp8 variant: fp8_quant_per_tensor of Q, K and V, then attn_fwd_fp8
+  3. the fp8 variant: per-tensor quantisation of Q, K and V (one
+     fp8_quant_per_tensor_multi call, two launches), then attn_fwd_fp8
   4. residual_diff over two bf16 [1, 4608, 3072] first-block residuals.
 ``value`` is the algorithmic attention work of the step (3 passes of
 4*B*H*N*N*D FLOP) divided by the step's wall time with every input already
@@ -174,9 +175,7 @@ def main():
         if ev is not None:
             ev[3].record()
         if "quant" in legs_on:
-            dta.fp8_quant_per_tensor(q, q8, ds[0:1])
-            dta.fp8_quant_per_tensor(k, k8, ds[1:2])
-            dta.fp8_quant_per_tensor(v, v8, ds[2:3])
+            dta.fp8_quant_per_tensor_multi([q, k, v], [q8, k8, v8], ds)
         if ev is not None:
             ev[4].record()
         if "fp8" in legs_on:

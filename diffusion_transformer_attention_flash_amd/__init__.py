@@ -10,8 +10,11 @@ kernels; there is no fallback path -- a missing library raises.
     attn_merge(o_parts, lse_parts)        -> (o, lse)
     residual_diff(a, b)                   -> device float32 scalar
     fp8_quant_per_tensor(x)               -> (x8 uint8, descale float32[1])
+    fp8_quant_per_tensor_multi([q, k, v]) -> ([q8, k8, v8], descale float32[3])
     attn_fwd_fp8(q8, k8, v8, descale, scale) -> (o, lse)
 """
+
+import ctypes
 
 import torch
 
@@ -21,7 +24,7 @@ from ._lib import DtaError  # noqa: F401
 __all__ = ["attn_fwd", "attn_merge", "attn_fwd_accum", "attn_merge_into", "residual_diff",
            "fbcache_step", "seq_concat", "seq_split", "head_concat", "head_split",
            "fp8_quant_rows_pow2", "attn_fwd_fp8_rows", "attn_fwd_fp8_rows_v",
-           "fp8_quant_per_tensor",
+           "fp8_quant_per_tensor", "fp8_quant_per_tensor_multi",
            "attn_fwd_fp8", "workspace", "DtaError"]
 
 _workspaces = {}
@@ -287,6 +290,47 @@ def fp8_quant_per_tensor(x, x8=None, descale=None):
                                          _ptr(ws), ctypes_ptr(_stream(x)))
     _lib.check("fp8_quant_per_tensor", st)
     return x8, descale
+
+
+def fp8_quant_per_tensor_multi(xs, x8s=None, descale=None):
+    """Per-tensor E4M3FN quantisation of up to four bf16 tensors (e.g. Q, K, V)
+    in two launches -> (list of x8 uint8 codes, descale f32[len(xs)]); codes and
+    scales equal fp8_quant_per_tensor's for each tensor."""
+    xs = list(xs)
+    if not 1 <= len(xs) <= 4:
+        raise ValueError("fp8_quant_per_tensor_multi takes 1 to 4 tensors")
+    dev = xs[0].device
+    for i, x in enumerate(xs):
+        _need(x, "xs[%d]" % i, torch.bfloat16)
+        if x.device != dev:
+            raise ValueError("all tensors must be on one device")
+    if x8s is None:
+        x8s = [torch.empty(x.shape, dtype=torch.uint8, device=dev) for x in xs]
+    else:
+        x8s = list(x8s)
+        if len(x8s) != len(xs):
+            raise ValueError("x8s must match xs")
+        for i, (x, x8) in enumerate(zip(xs, x8s)):
+            _need(x8, "x8s[%d]" % i, torch.uint8)
+            if x8.numel() != x.numel():
+                raise ValueError("x8s[%d] must have xs[%d]'s element count" % (i, i))
+    if descale is None:
+        descale = torch.empty((len(xs),), dtype=torch.float32, device=dev)
+    else:
+        _need(descale, "descale", torch.float32)
+        if descale.numel() < len(xs):
+            raise ValueError("descale needs one float per tensor")
+    n = len(xs)
+    xp = (ctypes.c_void_p * n)(*[x.data_ptr() for x in xs])
+    x8p = (ctypes.c_void_p * n)(*[t.data_ptr() for t in x8s])
+    ns = (ctypes.c_int64 * n)(*[x.numel() for x in xs])
+    ws = workspace(dev)
+    st = _lib.lib().fp8_quant_per_tensor_multi(n, ctypes.cast(xp, ctypes.c_void_p),
+                                               ctypes.cast(ns, ctypes.c_void_p),
+                                               ctypes.cast(x8p, ctypes.c_void_p), _ptr(descale),
+                                               _ptr(ws), ctypes_ptr(_stream(xs[0])))
+    _lib.check("fp8_quant_per_tensor_multi", st)
+    return x8s, descale
 
 
 def attn_fwd_fp8(q8, k8, v8, descale, scale=None, o=None, lse=None):

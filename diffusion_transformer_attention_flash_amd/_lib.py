@@ -24,6 +24,7 @@ SIGNATURES = {
     "residual_diff": (_I, [_P, _P, _I64, _P, _P, _P]),
     "fbcache_step": (_I, [_P, _P, _I64, _F, _P, _P, _I64, _P, _P, _P, _P]),
     "fp8_quant_per_tensor": (_I, [_P, _I64, _P, _P, _P, _P]),
+    "fp8_quant_per_tensor_multi": (_I, [_I, _P, _P, _P, _P, _P, _P]),
     "attn_fwd_fp8": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P]),
     "fp8_quant_rows_pow2": (_I, [_P, _I64, _I, _P, _P, _P]),
     "attn_fwd_fp8_rows": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P]),

@@ -6,7 +6,9 @@
 // * fp8_quant_rows_pow2 -- row-wise E4M3 quantisation with one power-of-two
 //   scale per row (the same section's more accurate option).
 // * fp8_quant_per_tensor -- per-tensor dynamic E4M3FN quantisation, scale
-//   amax|x|/448 (ParaAttention guide, section "fp8 quantization").
+//   amax|x|/448 (ParaAttention guide, section "fp8 quantization"), and
+//   fp8_quant_per_tensor_multi, the same for up to four tensors (Q, K, V) in
+//   the same two launches.
 //
 // The two grid-wide reductions (residual sums, fp8 amax) are HBM-bound scans.
 // A fixed grid of kRedBlocks workgroups strides over the tensor in 16-byte
@@ -20,6 +22,8 @@
 // the XCD, and one per workgroup costs more than the scan itself. The results
 // are independent of scheduling and bitwise reproducible, and the workspace
 // needs no initialisation.
+
+#include <algorithm>
 
 #include "common.h"
 
@@ -170,13 +174,26 @@ __device__ __forceinline__ uint32_t amax_bits(uint32_t w, uint32_t m) {
   return max(m, max(w & 0x7FFFu, (w >> 16) & 0x7FFFu));
 }
 
-__global__ __launch_bounds__(256) void amax_kernel(
-    const uint16_t* __restrict__ x, int64_t n, uint32_t* __restrict__ part) {
+// Up to kQuantMax tensors of one per-tensor quantisation call. Workgroups
+// are assigned tensor by tensor: blocks [t * per, (t + 1) * per) serve tensor
+// t, so every tensor keeps the grid a single-tensor call would use.
+constexpr int kQuantMax = 4;
+static_assert(kQuantMax * kRedBlocks * sizeof(uint32_t) <= kWsBytes, "amax partials fit ws");
+struct QuantTable {
+  const uint16_t* x[kQuantMax];
+  uint8_t* x8[kQuantMax];
+  int64_t n[kQuantMax];
+};
+
+__global__ __launch_bounds__(256) void amax_kernel(QuantTable tab, uint32_t* __restrict__ part) {
+  const int ti = blockIdx.x / kRedBlocks, lb = blockIdx.x - ti * kRedBlocks;
+  const uint16_t* __restrict__ x = tab.x[ti];
+  const int64_t n = tab.n[ti];
   const int64_t n8 = n >> 3;
-  const int64_t stride = (int64_t)gridDim.x * 256;
+  const int64_t stride = (int64_t)kRedBlocks * 256;
   const u32x4* x4 = reinterpret_cast<const u32x4*>(x);
   uint32_t m = 0;
-  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  int64_t i = (int64_t)lb * 256 + threadIdx.x;
   for (; i + stride < n8; i += 2 * stride) {
     const u32x4 v0 = x4[i], v1 = x4[i + stride];
 #pragma unroll
@@ -187,7 +204,7 @@ __global__ __launch_bounds__(256) void amax_kernel(
 #pragma unroll
     for (int e = 0; e < 4; ++e) m = amax_bits(v0[e], m);
   }
-  if (blockIdx.x == 0 && threadIdx.x < (n & 7))
+  if (lb == 0 && threadIdx.x < (n & 7))
     m = max(m, (uint32_t)(x[(n8 << 3) + threadIdx.x] & 0x7FFFu));
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
@@ -196,7 +213,7 @@ __global__ __launch_bounds__(256) void amax_kernel(
   __syncthreads();
   if (threadIdx.x == 0) {
     const uint32_t bm = max(max(sm[0], sm[1]), max(sm[2], sm[3]));
-    part[blockIdx.x] = bm;
+    part[ti * kRedBlocks + lb] = bm;
   }
 }
 
@@ -206,17 +223,18 @@ __device__ __forceinline__ float fp8_in(float x, float s) {
   return fminf(fmaxf(__fdiv_rn(x, s), -448.0f), 448.0f);
 }
 
-// Every workgroup first reduces the kRedBlocks partial maxima itself (one
-// 16-byte load per thread, from L2) instead of a one-workgroup finish launch;
-// workgroup 0 publishes the scale for later kernels.
+// Every workgroup first reduces its tensor's kRedBlocks partial maxima itself
+// (one 16-byte load per thread, from L2) instead of a one-workgroup finish
+// launch; the first workgroup of each tensor publishes that tensor's scale.
+// Workgroups [t * per, (t + 1) * per) cast tensor t.
 __global__ __launch_bounds__(256) void fp8_cast_kernel(
-    const uint16_t* __restrict__ x, int64_t n, uint8_t* __restrict__ x8,
-    const uint32_t* __restrict__ part, float* __restrict__ descale) {
+    QuantTable tab, int per, const uint32_t* __restrict__ part, float* __restrict__ descale) {
   static_assert(kRedBlocks == 4 * 256, "one 16-byte load of partials per thread");
+  const int ti = blockIdx.x / per, lb = blockIdx.x - ti * per;
   __shared__ uint32_t sm[4];
   __shared__ float s_sh;
   {
-    const u32x4 pv = reinterpret_cast<const u32x4*>(part)[threadIdx.x];
+    const u32x4 pv = reinterpret_cast<const u32x4*>(part + ti * kRedBlocks)[threadIdx.x];
     uint32_t r = max(max(pv[0], pv[1]), max(pv[2], pv[3]));
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) r = max(r, (uint32_t)__shfl_xor((int)r, off, 64));
@@ -227,15 +245,18 @@ __global__ __launch_bounds__(256) void fp8_cast_kernel(
       const float amax = bf16_bits_to_f32(bm);
       const float sc = (amax == 0.f) ? 1.0f : __fdiv_rn(amax, 448.0f);
       s_sh = sc;
-      if (blockIdx.x == 0) *descale = sc;
+      if (lb == 0) descale[ti] = sc;
     }
     __syncthreads();
   }
   const float s = s_sh;
+  const uint16_t* __restrict__ x = tab.x[ti];
+  uint8_t* __restrict__ x8 = tab.x8[ti];
+  const int64_t n = tab.n[ti];
   const int64_t n8 = n >> 3;
-  const int64_t stride = (int64_t)gridDim.x * 256;
+  const int64_t stride = (int64_t)per * 256;
   const u32x4* x4 = reinterpret_cast<const u32x4*>(x);
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += stride) {
+  for (int64_t i = (int64_t)lb * 256 + threadIdx.x; i < n8; i += stride) {
     const u32x4 v = x4[i];
     u32x2 r;
 #pragma unroll
@@ -251,7 +272,7 @@ __global__ __launch_bounds__(256) void fp8_cast_kernel(
     }
     *reinterpret_cast<u32x2*>(x8 + i * 8) = r;
   }
-  if (blockIdx.x == 0 && threadIdx.x < (n & 7)) {
+  if (lb == 0 && threadIdx.x < (n & 7)) {
     const int64_t t = (n8 << 3) + threadIdx.x;
     const float y = fp8_in(bf16_bits_to_f32(x[t]), s);
     x8[t] = (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(y, 0.f, 0, false) & 0xFF);
@@ -352,21 +373,48 @@ extern "C" int fbcache_step(const void* r, const void* r_prev, int64_t n, float 
   return hipGetLastError() == hipSuccess ? DTA_OK : DTA_ELAUNCH;
 }
 
+// Both per-tensor entry points: amax partials of every tensor in one launch,
+// then every tensor's cast in one launch.
+static int launch_quant(const QuantTable& tab, int count, float* descale, void* ws,
+                        hipStream_t stream) {
+  uint32_t* part = static_cast<uint32_t*>(ws);
+  hipLaunchKernelGGL(amax_kernel, dim3(count * kRedBlocks), dim3(256), 0, stream, tab, part);
+  if (hipGetLastError() != hipSuccess) return DTA_ELAUNCH;
+  int64_t want = 1;
+  for (int t = 0; t < count; ++t)
+    want = std::max<int64_t>(want, ((tab.n[t] >> 3) + 255) / 256);
+  const int per = (int)(want < 4096 ? want : 4096);
+  hipLaunchKernelGGL(fp8_cast_kernel, dim3(count * per), dim3(256), 0, stream, tab, per, part,
+                     descale);
+  return hipGetLastError() == hipSuccess ? DTA_OK : DTA_ELAUNCH;
+}
+
 extern "C" int fp8_quant_per_tensor(const void* x, int64_t n, void* x8,
                                     float* descale, void* ws, hipStream_t stream) {
   if (!x || !x8 || !descale || !ws || n < 1) return DTA_EINVAL;
   if (!al16(x) || !al16(x8) || !al16(ws) || (reinterpret_cast<uintptr_t>(descale) & 3))
     return DTA_EALIGN;
-  uint32_t* part = static_cast<uint32_t*>(ws);
-  hipLaunchKernelGGL(amax_kernel, dim3(kRedBlocks), dim3(256), 0, stream,
-                     static_cast<const uint16_t*>(x), n, part);
-  if (hipGetLastError() != hipSuccess) return DTA_ELAUNCH;
-  const int64_t want = ((n >> 3) + 255) / 256;
-  const unsigned grid = (unsigned)(want < 1 ? 1 : (want < 4096 ? want : 4096));
-  hipLaunchKernelGGL(fp8_cast_kernel, dim3(grid), dim3(256), 0, stream,
-                     static_cast<const uint16_t*>(x), n, static_cast<uint8_t*>(x8), part,
-                     descale);
-  return hipGetLastError() == hipSuccess ? DTA_OK : DTA_ELAUNCH;
+  QuantTable tab = {};
+  tab.x[0] = static_cast<const uint16_t*>(x);
+  tab.x8[0] = static_cast<uint8_t*>(x8);
+  tab.n[0] = n;
+  return launch_quant(tab, 1, descale, ws, stream);
+}
+
+extern "C" int fp8_quant_per_tensor_multi(int count, const void* const* x, const int64_t* n,
+                                          void* const* x8, float* descale, void* ws,
+                                          hipStream_t stream) {
+  if (count < 1 || count > kQuantMax || !x || !n || !x8 || !descale || !ws) return DTA_EINVAL;
+  QuantTable tab = {};
+  for (int t = 0; t < count; ++t) {
+    if (!x[t] || !x8[t] || n[t] < 1) return DTA_EINVAL;
+    if (!al16(x[t]) || !al16(x8[t])) return DTA_EALIGN;
+    tab.x[t] = static_cast<const uint16_t*>(x[t]);
+    tab.x8[t] = static_cast<uint8_t*>(x8[t]);
+    tab.n[t] = n[t];
+  }
+  if (!al16(ws) || (reinterpret_cast<uintptr_t>(descale) & 3)) return DTA_EALIGN;
+  return launch_quant(tab, count, descale, ws, stream);
 }
 
 extern "C" int fp8_quant_rows_pow2(const void* x, int64_t rows, int row_len, void* x8,

@@ -194,6 +194,24 @@ int fp8_quant_per_tensor(const void* x, int64_t n, void* x8, float* descale,
                          void* ws, hipStream_t stream);
 
 /*
+ * fp8_quant_per_tensor_multi -- fp8_quant_per_tensor of up to four tensors
+ * (typically Q, K and V of one attention call) in the same two launches:
+ * one kernel writes every tensor's partial maxima, one casts every tensor.
+ * Tensor t gets exactly the codes and scale fp8_quant_per_tensor gives it.
+ * count    1..4
+ * x, n, x8 HOST arrays of count entries: device pointers to bf16 [n[t]]
+ *          (16-byte aligned), element counts n[t] >= 1, and device pointers
+ *          to uint8 [n[t]] (16-byte aligned, written)
+ * descale  device float[count], 4-byte aligned, written with the scales
+ * ws       as for residual_diff (dta_ws_bytes() covers four tensors)
+ * Returns DTA_OK, DTA_EINVAL (count out of range, a null pointer, a size
+ * < 1), DTA_EALIGN or DTA_ELAUNCH.
+ */
+int fp8_quant_per_tensor_multi(int count, const void* const* x, const int64_t* n,
+                               void* const* x8, float* descale, void* ws,
+                               hipStream_t stream);
+
+/*
  * attn_fwd_fp8 -- the fp8 dynamic-quantisation variant of attn_fwd: Q, K, V
  * are E4M3FN with per-tensor scales (as fp8_quant_per_tensor writes them);
  * S = scale * s_q s_k (Q8 . K8^T) on fp8 MFMA with float32 accumulation;
@@ -310,7 +328,7 @@ int attn_fwd_fp8_rows_v(const void* q8, const void* k8, const void* v8,
                         void* o, float* lse, int B, int H, int Nq, int Nkv, int D,
                         float scale, hipStream_t stream);
 
-/* Bytes of the workspace residual_diff and fp8_quant_per_tensor need. */
+/* Bytes of the workspace residual_diff and the per-tensor quantisers need. */
 size_t dta_ws_bytes(void);
 
 /* A static, human-readable name of a dta_status value. */

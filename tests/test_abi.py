@@ -162,6 +162,29 @@ def test_reductions_validation():
     assert lib.fp8_quant_per_tensor(GOOD, 10, ODD, GOOD, GOOD, None) == _lib.DTA_EALIGN
 
 
+def test_quant_multi_validation():
+    lib = _lib.lib()
+    P = ctypes.c_void_p
+    xs = (P * 3)(0x10000, 0x20000, 0x30000)
+    x8s = (P * 3)(0x40000, 0x50000, 0x60000)
+    ns = (ctypes.c_int64 * 3)(10, 20, 30)
+    cast = lambda a: ctypes.cast(a, P)
+    call = lambda cnt, x=xs, n=ns, x8=x8s, ds=GOOD, ws=GOOD: lib.fp8_quant_per_tensor_multi(
+        cnt, cast(x) if x is not None else None, cast(n) if n is not None else None,
+        cast(x8) if x8 is not None else None, ds, ws, None)
+    assert call(0) == _lib.DTA_EINVAL                       # count out of range
+    assert call(5) == _lib.DTA_EINVAL
+    assert call(3, x=None) == _lib.DTA_EINVAL
+    assert call(3, n=None) == _lib.DTA_EINVAL
+    assert call(3, ds=None) == _lib.DTA_EINVAL
+    assert call(3, ws=None) == _lib.DTA_EINVAL
+    assert call(3, n=(ctypes.c_int64 * 3)(10, 0, 30)) == _lib.DTA_EINVAL   # a size < 1
+    assert call(3, x=(P * 3)(0x10000, None, 0x30000)) == _lib.DTA_EINVAL   # a null tensor
+    assert call(3, x8=(P * 3)(0x40000, 0x50008, 0x60000)) == _lib.DTA_EALIGN
+    assert call(3, ds=ctypes.c_void_p(0x10002)) == _lib.DTA_EALIGN
+    assert call(3, ws=ODD) == _lib.DTA_EALIGN
+
+
 def test_binding_rejects_cpu_tensors():
     import torch
     import diffusion_transformer_attention_flash_amd as dta

@@ -81,3 +81,37 @@ def test_fp8_quant_zero_tensor_and_repeat():
     torch.cuda.synchronize()
     codes, s = oracle.quant_per_tensor(x)
     assert float(ds.item()) == s and (x8.cpu().numpy() == codes).all()
+
+
+@pytest.mark.parametrize("sizes", [[(1000003,), (7,), (3, 5, 64)], [(4097,)],
+                                   [(9,), (8,), (33, 17), (1, 2, 300, 128)]])
+def test_fp8_quant_multi_bit_exact(sizes):
+    """fp8_quant_per_tensor_multi gives every tensor the oracle's codes and
+    scale, as fp8_quant_per_tensor does, whatever the mix of sizes (ragged
+    tails, one tensor, four tensors, one all-zero tensor)."""
+    print("CASE quant multi", sizes, flush=True)
+    g = torch.Generator().manual_seed(len(sizes) * 100 + sum(len(s) for s in sizes))
+    xs = [(torch.randn(s, generator=g) * (3.0 ** i)).to(torch.bfloat16) for i, s in enumerate(sizes)]
+    if len(xs) == 4:
+        xs[1] = torch.zeros(sizes[1], dtype=torch.bfloat16)
+    x8s, ds = dta.fp8_quant_per_tensor_multi([x.to(DEV) for x in xs])
+    torch.cuda.synchronize()
+    for i, x in enumerate(xs):
+        codes, s = oracle.quant_per_tensor(x)
+        assert float(ds[i].item()) == s, i
+        got = x8s[i].cpu().numpy()
+        mism = int((got != codes).sum())
+        assert mism == 0, "tensor %d: %d of %d codes differ" % (i, mism, codes.size)
+
+
+def test_fp8_quant_multi_flux_qkv_matches_single():
+    """Q, K and V of the FLUX shape in one call: bitwise what three single
+    calls give."""
+    print("CASE quant multi flux", flush=True)
+    q, k, v = workloads.workload_qkv("flux_1024", device=DEV)
+    x8s, ds = dta.fp8_quant_per_tensor_multi([q, k, v])
+    singles = [dta.fp8_quant_per_tensor(t) for t in (q, k, v)]
+    torch.cuda.synchronize()
+    for i, (x8, d) in enumerate(singles):
+        assert torch.equal(x8s[i], x8), i
+        assert float(ds[i].item()) == float(d.item()), i
