@@ -112,7 +112,7 @@ def main():
     legs_on = set(["attn", "chunks", "merge", "quant", "fp8", "residual"]
                   if args.legs == "all" else args.legs.split(","))
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(the ring/Ulysses exchanges are out of scope); run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
