@@ -78,6 +78,23 @@ def test_fp8_flux_1024_sampled_rows():
     _check(o8, l8, q, k, v, q8, k8, v8, ds, c["D"] ** -0.5, rows=rows, what="fp8 flux")
 
 
+def test_fp8_video_length_sampled_rows():
+    """The HunyuanVideo 720p x 129-frame sequence length (119 056 tokens: 1861
+    K/V tiles, the last one 16 keys) on two heads of its recipe, 256 sampled
+    query rows per head: the longest K/V loop of the workloads, with its
+    running max, rare rescales and float32 row sums. Two heads keep the
+    oracle's quantisation of the whole tensors within seconds."""
+    c = workloads.CONFIGS["hunyuan_720p_129f"]
+    N, D = c["N"], c["D"]
+    print("CASE fp8 video length, 2 heads", flush=True)
+    q, k, v = workloads.make_qkv(c["config"], 1, 2, N, N, D, device=DEV)
+    q8, k8, v8, ds = _quant3(q, k, v)
+    o8, l8 = dta.attn_fwd_fp8(q8, k8, v8, ds, D ** -0.5)
+    torch.cuda.synchronize()
+    rows = workloads.sample_rows(c["config"], N, 256, c["n_text"])
+    _check(o8, l8, q, k, v, q8, k8, v8, ds, D ** -0.5, rows=rows, what="fp8 video length")
+
+
 @pytest.mark.parametrize("Nkv", [1, 40, 64, 65, 128, 150, 192, 256, 300, 320, 385])
 def test_fp8_attention_tile_counts(Nkv):
     """K/V lengths of 1 to 7 tiles of 64 keys, full and ragged last tile: the

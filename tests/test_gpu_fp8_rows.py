@@ -95,6 +95,24 @@ def test_attention_rows_flux_sampled():
     _check(o8, l8, q, k, v, q8, k8, v8, eq, ek, sv, c["D"] ** -0.5, rows=rows, what="fp8 rows flux")
 
 
+def _video_length_inputs():
+    # Two heads of the HunyuanVideo 720p x 129-frame recipe at its full
+    # sequence length (119 056 tokens: 1861 K/V tiles, the last one 16 keys).
+    c = workloads.CONFIGS["hunyuan_720p_129f"]
+    N, D = c["N"], c["D"]
+    q, k, v = workloads.make_qkv(c["config"], 1, 2, N, N, D, device=DEV)
+    return q, k, v, D ** -0.5, workloads.sample_rows(c["config"], N, 256, c["n_text"])
+
+
+def test_attention_rows_video_length_sampled():
+    print("CASE fp8 rows video length, 2 heads", flush=True)
+    q, k, v, scale, rows = _video_length_inputs()
+    q8, k8, v8, eq, ek, sv = _rows_path(q, k, v)
+    o8, l8 = dta.attn_fwd_fp8_rows(q8, k8, v8, eq, ek, sv, scale)
+    torch.cuda.synchronize()
+    _check(o8, l8, q, k, v, q8, k8, v8, eq, ek, sv, scale, rows=rows, what="fp8 rows video length")
+
+
 def test_uniform_exponents_match_per_tensor_bitwise():
     """With every row exponent equal, the MFMA operand scales 2^(eq+ek) and
     the per-tensor path's float factor s_q s_k = 2^(eq+ek) give the same
@@ -186,6 +204,16 @@ def test_attention_rows_v_flux_sampled():
     rows = workloads.sample_rows(c["config"], c["N"], 256, c["n_text"])
     _check_v(o8, l8, q, k, v, q8, k8, v8, eq, ek, ev, c["D"] ** -0.5, rows=rows,
              what="fp8 rows_v flux")
+
+
+def test_attention_rows_v_video_length_sampled():
+    print("CASE fp8 rows_v video length, 2 heads", flush=True)
+    q, k, v, scale, rows = _video_length_inputs()
+    q8, k8, v8, eq, ek, ev = _rows_v_path(q, k, v)
+    o8, l8 = dta.attn_fwd_fp8_rows_v(q8, k8, v8, eq, ek, ev, scale)
+    torch.cuda.synchronize()
+    _check_v(o8, l8, q, k, v, q8, k8, v8, eq, ek, ev, scale, rows=rows,
+             what="fp8 rows_v video length")
 
 
 def test_rows_v_uniform_scores_give_the_mean_of_v():
