@@ -8,10 +8,19 @@ kernels; there is no fallback path -- a missing library raises.
 
     attn_fwd(q, k, v, scale)              -> (o, lse)
     attn_merge(o_parts, lse_parts)        -> (o, lse)
+    attn_fwd_accum(q, k, v, o, lse)       one ring step, merged into (o, lse)
+    attn_merge_into(o, lse, o_part, lse_part)  pairwise in-place merge
     residual_diff(a, b)                   -> device float32 scalar
+    fbcache_step(r, r_prev, thr, hidden, cached) -> (diff, use_cache) on device
+    seq_concat / seq_split / head_concat / head_split   layout permutations
     fp8_quant_per_tensor(x)               -> (x8 uint8, descale float32[1])
     fp8_quant_per_tensor_multi([q, k, v]) -> ([q8, k8, v8], descale float32[3])
     attn_fwd_fp8(q8, k8, v8, descale, scale) -> (o, lse)
+    fp8_quant_rows_pow2(x)                -> (x8 uint8, e8m0 uint8 per row)
+    attn_fwd_fp8_rows / attn_fwd_fp8_rows_v   row-wise scaled fp8 attention
+
+The reductions share a small device workspace; the binding keeps one per
+(device, stream), so calls on different streams never share it.
 """
 
 import ctypes
@@ -52,19 +61,21 @@ def _ptr(t):
 
 
 def ctypes_ptr(addr):
-    import ctypes
     return ctypes.c_void_p(addr)
 
 
 def workspace(device):
-    """The reduction workspace of ``device`` (allocated once by torch)."""
+    """The reduction workspace of ``device`` for its current stream (allocated
+    once per (device, stream) by torch). Kernels on one stream run in order,
+    so they may share it; work on another stream gets its own."""
     device = torch.device(device)
     idx = device.index if device.index is not None else torch.cuda.current_device()
-    ws = _workspaces.get(idx)
+    key = (idx, torch.cuda.current_stream(idx).cuda_stream)
+    ws = _workspaces.get(key)
     if ws is None:
         nbytes = int(_lib.lib().dta_ws_bytes())
         ws = torch.zeros(nbytes, dtype=torch.uint8, device=torch.device("cuda", idx))
-        _workspaces[idx] = ws
+        _workspaces[key] = ws
     return ws
 
 

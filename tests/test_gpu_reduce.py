@@ -115,3 +115,38 @@ def test_fp8_quant_multi_flux_qkv_matches_single():
     for i, (x8, d) in enumerate(singles):
         assert torch.equal(x8s[i], x8), i
         assert float(ds[i].item()) == float(d.item()), i
+
+
+def test_reductions_on_two_streams():
+    """The binding gives each (device, stream) its own reduction workspace, so
+    residual_diff and the per-tensor quantiser issued on two streams at once
+    give the results of calls on one stream, bit for bit."""
+    print("CASE reductions on two streams", flush=True)
+    c = workloads.CONFIGS["flux_1024_fp8"]
+    a1, b1 = workloads.residual_pair(c["config"], c["residual_shape"], c["residual_noise"], device=DEV)
+    a2, b2 = workloads.residual_pair(c["config"] + 1, (1, 1000, 3072), 0.5, device=DEV)
+    g = torch.Generator(device=DEV).manual_seed(3)
+    x = torch.randn(1 << 22, generator=g, device=DEV).to(torch.bfloat16)
+    r1, r2 = dta.residual_diff(a1, b1).clone(), dta.residual_diff(a2, b2).clone()
+    x8, s = dta.fp8_quant_per_tensor(x)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    with torch.cuda.stream(s1):
+        ws1 = dta.workspace(DEV)
+    with torch.cuda.stream(s2):
+        ws2 = dta.workspace(DEV)
+    assert ws1.data_ptr() != ws2.data_ptr()
+    got = []
+    for _ in range(10):
+        with torch.cuda.stream(s1):
+            got.append(("r1", dta.residual_diff(a1, b1)))
+            got.append(("q", dta.fp8_quant_per_tensor(x)))
+        with torch.cuda.stream(s2):
+            got.append(("r2", dta.residual_diff(a2, b2)))
+    torch.cuda.synchronize()
+    assert r1.item() != r2.item()
+    for what, val in got:
+        if what == "q":
+            assert torch.equal(val[0], x8) and torch.equal(val[1], s)
+        else:
+            assert torch.equal(val, r1 if what == "r1" else r2), what
