@@ -193,3 +193,25 @@ def test_binding_rejects_cpu_tensors():
         dta.attn_fwd(q, q, q)
     with pytest.raises(ValueError):
         dta.residual_diff(q, q)
+
+
+def test_missing_library_raises(monkeypatch):
+    """No fallback: with the shared library absent the binding raises."""
+    monkeypatch.setattr(_lib, "LIB_PATH", os.path.join(ROOT, "no_such_dir", "libdta.so"))
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        _lib.lib()
+
+
+def test_host_tensors_are_rejected():
+    """The binding takes device tensors only; host tensors raise before any
+    library call (there is no CPU path)."""
+    import torch
+    import diffusion_transformer_attention_flash_amd as dta
+    q = torch.zeros(1, 1, 64, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        dta.attn_fwd(q, q, q)
+    with pytest.raises(ValueError, match="GPU"):
+        dta.residual_diff(q, q)
+    with pytest.raises(ValueError, match="GPU"):
+        dta.fp8_quant_per_tensor(q)
