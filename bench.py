@@ -15,7 +15,8 @@ attention shape (B=1, H=24, N=4608 = 512 text + 4096 image tokens, D=128):
 resident in HBM; the merge, quantisation and residual-diff kernels are
 inside the timed region. ``roofline`` reports the dominant kernel (bf16
 attn_fwd at the FLUX shape) from HIP events around each of its launches.
-The 119056-token HunyuanVideo shape is timed separately (``video``).
+The 119056-token HunyuanVideo shape is timed separately (``video``: bf16 and
+per-tensor fp8 attention).
 ``cpu_baseline`` times the float64 CPU oracle on a bounded sample.
 
 Prints ONE JSON line.
@@ -436,7 +437,24 @@ def main():
                  "ms": ms_v, "TFLOP/s": fv / (ms_v * 1e-3) / 1e12,
                  "frac_bf16_peak": fv / (ms_v * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                  "reps": len(ts)}
-        del qv, kv, vv, ov, lv
+        # The per-tensor fp8 attention at the same shape (quantisation outside
+        # the timed launches).
+        (q8v, k8v, v8v), dsv = dta.fp8_quant_per_tensor_multi([qv, kv, vv])
+        del qv, kv, vv
+        dta.attn_fwd_fp8(q8v, k8v, v8v, dsv, cv["D"] ** -0.5, o=ov, lse=lv)
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(max(1, args.video_reps)):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            dta.attn_fwd_fp8(q8v, k8v, v8v, dsv, cv["D"] ** -0.5, o=ov, lse=lv)
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        ms_v8 = sorted(ts)[len(ts) // 2]
+        video["fp8_per_tensor"] = {"ms": ms_v8, "TFLOP/s": fv / (ms_v8 * 1e-3) / 1e12,
+                                   "frac_fp8_peak": fv / (ms_v8 * 1e-3) / 1e12 / PEAK_FP8_TFLOPS}
+        del q8v, k8v, v8v, ov, lv
 
     cpu = None
     if not args.no_cpu_baseline:
