@@ -17,20 +17,22 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
-def _shapes(n, seed=20261203):
+def _shapes(n, seed=20261203, hi=600):
     rng = np.random.default_rng(seed)
     out = []
     for _ in range(n):
         B = int(rng.integers(1, 3))
         H = int(rng.integers(1, 4))
-        Nq = int(rng.integers(1, 600))
-        Nkv = int(rng.integers(1, 600))
+        Nq = int(rng.integers(1, hi))
+        Nkv = int(rng.integers(1, hi))
         D = int(rng.choice([64, 128]))
         out.append((B, H, Nq, Nkv, D))
     return out
 
 
-SHAPES = _shapes(8)
+# 8 short shapes, then 16 up to 2000 rows: several query tiles per head and
+# K/V loops of up to 32 tiles, each with its own ragged tails.
+SHAPES = _shapes(8) + _shapes(16, seed=20261204, hi=2000)
 
 
 @pytest.mark.parametrize("i", range(len(SHAPES)))
