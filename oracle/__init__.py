@@ -38,7 +38,8 @@ What it computes, each written from the plain definition (numpy, float64):
                          power-of-two scale per token for Q and K.
 * ``attention_fp8_rows_v`` -- the same with V's per-token scale folded into
                          the probabilities and one power-of-two P scale per
-                         (query, 32 consecutive keys).
+                         (query, block of consecutive keys); the block size
+                         is an argument.
 
 Every function is pinned by tests in ``tests/test_oracle_pins.py`` against
 mathematics it does not share code with (arbitrary-precision brute force,
@@ -48,13 +49,13 @@ closed forms, invariants, a library float8 cast). None is "parity unpinned".
 from .attention import attention, merge, softmax_rows
 from .residual import fbcache_step, residual_diff
 from . import layout
-from .fp8 import (E4M3_MAX, e4m3_decode, e4m3_encode, quant_per_tensor, quant_rows_pow2,
-                  attention_fp8_rows, attention_fp8_rows_v, p_block_ids, pow2_exponent,
-                  quant_p_blocks, attention_fp8)
+from .fp8 import (E4M3_MAX, e4m3_decode, e4m3_encode, e4m3_round, quant_per_tensor,
+                  quant_rows_pow2, attention_fp8_rows, attention_fp8_rows_v, p_block_ids,
+                  p_block_exponents, pow2_exponent, quant_p_blocks, attention_fp8)
 
 __all__ = [
     "attention", "merge", "softmax_rows", "residual_diff", "fbcache_step", "layout", "E4M3_MAX",
-    "e4m3_decode", "e4m3_encode", "quant_per_tensor", "attention_fp8",
+    "e4m3_decode", "e4m3_encode", "e4m3_round", "quant_per_tensor", "attention_fp8",
     "quant_rows_pow2", "attention_fp8_rows", "attention_fp8_rows_v", "p_block_ids",
-    "pow2_exponent", "quant_p_blocks",
+    "p_block_exponents", "pow2_exponent", "quant_p_blocks",
 ]

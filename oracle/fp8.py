@@ -67,6 +67,25 @@ def e4m3_encode(x):
     return code.astype(np.uint8)
 
 
+def e4m3_round(x):
+    """The float64 value of the E4M3FN number nearest to each x (ties to the
+    even mantissa), saturating at +-448; NaN stays NaN. Equal to
+    ``e4m3_decode(e4m3_encode(x))``, computed from the format's spacing
+    instead of a table search: a binade [2^(e-1), 2^e) at or above 2^-6
+    holds 8 values 2^(e-4) apart (3 mantissa bits), and below 2^-6 the
+    subnormals are 2^-9 apart, so the nearest value is an integer multiple
+    of that spacing (numpy's round is half-to-even, and an even multiple is
+    an even mantissa, also where a tie rounds up into the next binade).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    _, e = np.frexp(a)                       # a in [2^(e-1), 2^e)
+    spacing = np.ldexp(1.0, np.maximum(e - 4, -9))
+    with np.errstate(invalid="ignore"):
+        r = np.minimum(np.round(a / spacing) * spacing, E4M3_MAX)
+    return np.where(np.isnan(x), np.nan, np.copysign(r, x))
+
+
 def quant_per_tensor(x):
     """Per-tensor dynamic quantisation of ``x`` to E4M3FN.
 
@@ -166,39 +185,49 @@ def _attention_p8(q, k, v, scale, rows):
             m = s.max(axis=1, keepdims=True)
             p = np.exp(s - m)
             l = p.sum(axis=1, keepdims=True)
-            p8 = e4m3_decode(e4m3_encode(E4M3_MAX * p))
+            p8 = e4m3_round(E4M3_MAX * p)
             o[b, h] = (p8 @ v[b, h]) / (E4M3_MAX * l)
             lse[b, h] = m[:, 0] + np.log(l[:, 0])
     return o, lse
 
 
-def p_block_ids(nkv, block=32):
-    """Block of each key for the per-block P scales of ``attention_fp8_rows_v``:
-    32 consecutive keys, key j in block j // 32. (The pages leave the P
-    granularity open. gfx950's fp8 MFMA applies one operand scale to each 32
-    consecutive k of a row or column, measured with single-byte probes, so a
-    block of 32 consecutive keys is one operand scale of the P.V product.)
-    """
+def p_block_ids(nkv, block):
+    """Block label of each of ``nkv`` keys for per-block P scales: ``block``
+    consecutive keys share a label, key j is in block j // block (the last
+    block may be shorter). The pages leave the granularity of P's scale
+    open, so the block size is a parameter of the definition."""
+    block = int(block)
+    if block < 1:
+        raise ValueError("block must be >= 1")
     return np.arange(int(nkv)) // block
+
+
+def p_block_exponents(pv, blocks):
+    """One power-of-two exponent per (row, block) of the non-negative values
+    pv [rows, Nkv]: e = pow2_exponent(the block's largest value), so that
+    value lands in (224, 448] * 2^e (e = 0 for an all-zero block). ``blocks``
+    labels the keys 0, 0, .., 1, 1, .. in runs (as ``p_block_ids`` does).
+    Returns e of shape [rows, n_blocks]."""
+    pv = np.asarray(pv, dtype=np.float64)
+    blocks = np.asarray(blocks)
+    starts = np.flatnonzero(np.r_[True, blocks[1:] != blocks[:-1]])
+    if not np.array_equal(blocks[starts], np.arange(starts.size)):
+        raise ValueError("blocks must label consecutive runs 0, 1, 2, ...")
+    bmax = np.maximum.reduceat(pv, starts, axis=1)
+    return pow2_exponent(bmax)
 
 
 def quant_p_blocks(pv, blocks):
     """E4M3 codes of the probabilities pv [rows, Nkv] with one power-of-two
-    scale per (row, block): 2^e with e = pow2_exponent(max of the block), so
-    the block's largest value lands in [224, 448]. Returns (codes, e) with e
-    of shape [rows, n_blocks]."""
+    scale per (row, block): 2^e with e from ``p_block_exponents``. Returns
+    (codes, e) with e of shape [rows, n_blocks]."""
     pv = np.asarray(pv, dtype=np.float64)
-    blocks = np.asarray(blocks)
-    nb = int(blocks.max()) + 1
-    e = np.zeros((pv.shape[0], nb), dtype=np.int64)
-    for b in range(nb):
-        idx = np.nonzero(blocks == b)[0]
-        e[:, b] = pow2_exponent(pv[:, idx].max(axis=1))
-    codes = e4m3_encode(pv * np.ldexp(1.0, -e[:, blocks]))
+    e = p_block_exponents(pv, blocks)
+    codes = e4m3_encode(pv * np.ldexp(1.0, -e[:, np.asarray(blocks)]))
     return codes, e
 
 
-def attention_fp8_rows_v(q8, k8, v8, q_e8m0, k_e8m0, v_e8m0, scale, rows=None):
+def attention_fp8_rows_v(q8, k8, v8, q_e8m0, k_e8m0, v_e8m0, scale, *, block, rows=None):
     """Row-wise fp8 attention with per-token scales for Q, K and V and
     per-block scales for P (ParaAttention guide, section "fp8 quantization":
     row-wise scaling as the more accurate option).
@@ -206,12 +235,14 @@ def attention_fp8_rows_v(q8, k8, v8, q_e8m0, k_e8m0, v_e8m0, scale, rows=None):
     Q, K and V are E4M3 codes with one power-of-two scale per token (E8M0
     bytes [B,H,N]). With p = exp(s - m) as in ``attention_fp8``, V's scale is
     folded into the probabilities, pv_j = p_j * 2^(ev_j - 127), which are
-    quantised to E4M3 with one power-of-two scale per (query, block of 32
-    consecutive keys, ``p_block_ids``) before the product with V's codes:
-    O = sum_j P^_j * v8_j / sum_j p_j, LSE = m + ln sum_j p_j, where P^ is the
-    dequantised pv. A block shares one scale, so inside a block pv values
-    more than E4M3's span (about 2^17) below the block maximum round to zero;
-    a per-tensor V scale has the same limit over the whole tensor.
+    rounded to E4M3 with one power-of-two scale per (query, block of
+    ``block`` consecutive keys; ``p_block_ids``) before the product with V's
+    codes: O = sum_j P^_j * v8_j / sum_j p_j, LSE = m + ln sum_j p_j, where
+    P^ is the dequantised pv. ``block`` is required: the pages do not fix the
+    granularity (1 gives every key its own scale; Nkv or more one scale per
+    query row). A block shares one scale, so inside a block pv values more
+    than E4M3's span (about 2^17) below the block maximum round to zero; a
+    per-tensor V scale has the same limit over the whole tensor.
     """
     q = e4m3_decode(np.asarray(q8)) * np.ldexp(1.0, np.asarray(q_e8m0, dtype=np.int64) - 127)[..., None]
     k = e4m3_decode(np.asarray(k8)) * np.ldexp(1.0, np.asarray(k_e8m0, dtype=np.int64) - 127)[..., None]
@@ -224,7 +255,7 @@ def attention_fp8_rows_v(q8, k8, v8, q_e8m0, k_e8m0, v_e8m0, scale, rows=None):
     if rows is not None:
         q = q[:, :, np.asarray(rows, dtype=np.int64), :]
     nq = q.shape[2]
-    blocks = p_block_ids(nkv)
+    blocks = p_block_ids(nkv, block)
     o = np.empty((B, H, nq, D), dtype=np.float64)
     lse = np.empty((B, H, nq), dtype=np.float64)
     for b in range(B):
@@ -234,9 +265,8 @@ def attention_fp8_rows_v(q8, k8, v8, q_e8m0, k_e8m0, v_e8m0, scale, rows=None):
             p = np.exp(s - m)
             l = p.sum(axis=1, keepdims=True)
             pv = p * np.ldexp(1.0, ev[b, h])[None, :]
-            codes, e = quant_p_blocks(pv, blocks)
-            pq = e4m3_decode(codes) * np.ldexp(1.0, e[:, blocks])
+            f = np.ldexp(1.0, p_block_exponents(pv, blocks))[:, blocks]
+            pq = e4m3_round(pv / f) * f
             o[b, h] = (pq @ vq[b, h]) / l
             lse[b, h] = m[:, 0] + np.log(l[:, 0])
     return o, lse
-

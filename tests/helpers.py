@@ -50,3 +50,117 @@ def assert_bf16_attention(o, lse, o_ref, lse_ref, what=""):
     assert e_l <= LSE_ABS, msg
     assert r <= O_REL_L2, msg
     return e_o, e_l, r
+
+
+# ---- elementwise error bound of the fp8 kernels' P rounding ----------------
+#
+# The fp8 kernels round the probabilities to E4M3 before the P.V product
+# (include/dta.h): attn_fwd_fp8 and attn_fwd_fp8_rows take
+# P8 = e4m3(108 p') with p' = exp(s - m'), m' a reference max that never
+# exceeds the row max and trails it by at most 2 bits at the end;
+# attn_fwd_fp8_rows_v takes one power-of-two scale 2^e per (query, block of
+# 32 consecutive keys) with the block's largest V-scaled probability in
+# (224, 448] * 2^e. E4M3 rounds a value x with |e4m3(x) - x| <= 2^-4 |x|
+# (normal range: 3 mantissa bits, half an ulp) or <= 2^-10 (below 2^-6: half
+# the subnormal spacing 2^-9), so |e4m3(x) - x| <= 2^-4 |x| + 2^-10. Carried
+# back to the row's exact softmax weights w_j = p_j / l (p_j = exp(s_j - m),
+# l = sum_j p_j >= 1), every earlier, lower reference only shrinks the
+# absolute term, and
+#   per scale sigma:  |O - O*| <= 2^-4 sum_j w_j |v_j| + 2^-10 / (sigma l) sum_j |v_j|
+#   per block:        |O - O*| <= 2^-4 sum_j w_j |v_j|
+#                                 + 2^-10 / (224 l) sum_j bmax_B(j) |v8_j|
+# with O* exact attention on the dequantised inputs, v_j the dequantised V
+# and v8_j its E4M3 value (V's per-token scale folded into pv = p 2^ev).
+# Added: one bf16 rounding of O (2^-9 relative, taken twice) and float32
+# accumulation over Nkv terms (2 Nkv 2^-24 relative to sum_j w_j |v_j|).
+KERNEL_P_SCALE = 108.0
+KERNEL_P_BLOCK = 32
+
+
+def _fp8_bound_head(qd, kd, vd, scale, p_scale=None, vq=None, ev=None, block=None):
+    s = float(scale) * (qd @ kd.T)
+    m = s.max(axis=1, keepdims=True)
+    p = np.exp(s - m)
+    l = p.sum(axis=1, keepdims=True)
+    w = p / l
+    o_star = w @ vd
+    a = w @ np.abs(vd)
+    nkv = kd.shape[0]
+    if block is None:
+        flush = (2.0 ** -10 / p_scale) * np.abs(vd).sum(axis=0)[None, :] / l
+    else:
+        pv = p * np.exp2(ev.astype(np.float64))[None, :]
+        starts = np.arange(0, nkv, block)
+        bmax = np.maximum.reduceat(pv, starts, axis=1)
+        rep = np.repeat(bmax, np.diff(np.r_[starts, nkv]), axis=1)
+        flush = (2.0 ** -10 / 224.0) * (rep @ np.abs(vq)) / l
+    gamma = 2.0 * nkv * 2.0 ** -24
+    bound = 2.0 ** -4 * a + flush + 2.0 ** -8 * np.abs(o_star) + gamma * (a + np.abs(o_star)) + 1e-7
+    return o_star, bound
+
+
+def fp8_p_rounding_bound(qd, kd, vd, scale, p_scale=None, vq=None, ev=None, block=None,
+                         rows=None):
+    """(O*, bound), both [B,H,rows,D]: exact attention O* on the dequantised
+    float64 inputs qd [B,H,Nq,D], kd/vd [B,H,Nkv,D] and the elementwise bound
+    above on |O_kernel - O*|. Per-scale form with ``p_scale``; per-block form
+    with ``block``, ``vq`` (V's E4M3 values, [B,H,Nkv,D]) and ``ev`` (V's
+    per-token exponents, [B,H,Nkv])."""
+    qd, kd, vd = to64(qd), to64(kd), to64(vd)
+    if rows is not None:
+        qd = qd[:, :, np.asarray(rows, dtype=np.int64)]
+    B, H, nq, D = qd.shape
+    o = np.empty((B, H, nq, D))
+    bd = np.empty((B, H, nq, D))
+    for b in range(B):
+        for h in range(H):
+            o[b, h], bd[b, h] = _fp8_bound_head(
+                qd[b, h], kd[b, h], vd[b, h], scale, p_scale,
+                None if vq is None else vq[b, h], None if ev is None else ev[b, h], block)
+    return o, bd
+
+
+def assert_within_bound(o, o_star, bound, what=""):
+    d = np.abs(to64(o) - o_star)
+    ratio = (d / bound).max()
+    msg = "%s: elementwise |O - O*| / bound max %.3f (max err %.3e)" % (what, ratio, d.max())
+    print(msg)
+    assert np.isfinite(d).all() and ratio <= 1.0, msg
+    return ratio
+
+
+def deq_per_tensor(codes, s):
+    """float64 values of E4M3 codes (numpy or torch) with one scale s."""
+    if isinstance(codes, torch.Tensor):
+        codes = codes.cpu().numpy()
+    import oracle
+    return oracle.e4m3_decode(codes) * float(s)
+
+
+def deq_rows(codes, e8m0):
+    """float64 values of E4M3 codes [..., N, D] with one E8M0 exponent byte
+    per row [..., N] (scale 2^(byte - 127))."""
+    if isinstance(codes, torch.Tensor):
+        codes = codes.cpu().numpy()
+    if isinstance(e8m0, torch.Tensor):
+        e8m0 = e8m0.cpu().numpy()
+    import oracle
+    e = np.asarray(e8m0, dtype=np.int64).reshape(codes.shape[:-1]) - 127
+    return oracle.e4m3_decode(codes) * np.exp2(e.astype(np.float64))[..., None]
+
+
+def head_groups(rows, H):
+    """(head slice, rows or None) pairs: one group of every head and row
+    when ``rows`` is None, else one group per head with its own rows
+    (``rows`` [H, r] as workloads.sample_rows_per_head returns)."""
+    if rows is None:
+        return [(slice(None), None)]
+    return [(slice(h, h + 1), np.asarray(rows[h])) for h in range(H)]
+
+
+def take_rows(t, hs, r):
+    """Head slice hs and (optionally) rows r of a [B,H,N,...] tensor, on the CPU."""
+    t = t[:, hs]
+    if r is not None:
+        t = t[:, :, torch.from_numpy(r).to(t.device)]
+    return t.cpu()

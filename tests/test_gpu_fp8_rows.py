@@ -9,8 +9,10 @@ import torch
 import diffusion_transformer_attention_flash_amd as dta
 import oracle
 import workloads
-from helpers import (FP8_O_MEAN_ABS, FP8_REL_L2_VS_BF16, FP8_REL_L2_VS_DEQUANT, LSE_ABS,
-                     rel_l2, to64)
+from helpers import (FP8_O_MEAN_ABS, FP8_REL_L2_VS_BF16, FP8_REL_L2_VS_DEQUANT,
+                     KERNEL_P_BLOCK, KERNEL_P_SCALE, LSE_ABS, assert_bf16_attention,
+                     assert_within_bound, deq_per_tensor, deq_rows, fp8_p_rounding_bound,
+                     head_groups, rel_l2, take_rows, to64)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -52,25 +54,41 @@ def _rows_path(q, k, v):
     return q8, k8, v8, eq, ek, sv
 
 
-def _check(o8, l8, q, k, v, q8, k8, v8, eq, ek, sv, scale, rows=None, what=""):
-    o_dq, l_dq = oracle.attention_fp8_rows(q8.cpu().numpy(), k8.cpu().numpy(), v8.cpu().numpy(),
-                                           eq.cpu().numpy(), ek.cpu().numpy(), float(sv.item()),
-                                           scale, rows=rows)
-    o_bf, _ = oracle.attention(q.cpu(), k.cpu(), v.cpu(), scale, rows=rows)
-    if rows is not None:
-        rt = torch.from_numpy(rows).to(o8.device)
-        o8, l8 = o8[:, :, rt], l8[:, :, rt]
-    o8, l8 = to64(o8), to64(l8)
+def _gates(acc, what):
+    a = {key: np.concatenate(val, axis=1) for key, val in acc.items()}
+    o8, l8 = a["o"], a["l"]
     assert np.isfinite(o8).all() and np.isfinite(l8).all()
-    mean_abs = np.abs(o8 - o_bf).mean()
-    r_bf, r_dq = rel_l2(o8, o_bf), rel_l2(o8, o_dq)
-    e_l = np.abs(l8 - l_dq).max()
+    mean_abs = np.abs(o8 - a["bf"]).mean()
+    r_bf, r_dq = rel_l2(o8, a["bf"]), rel_l2(o8, a["dq"])
+    e_l = np.abs(l8 - a["ldq"]).max()
     msg = "%s: O mean-abs %.3e, rel-L2 %.3e (bf16) %.3e (dequant), LSE %.3e" % (
         what, mean_abs, r_bf, r_dq, e_l)
     print(msg)
     assert mean_abs <= FP8_O_MEAN_ABS and r_bf <= FP8_REL_L2_VS_BF16, msg
     assert r_dq <= FP8_REL_L2_VS_DEQUANT and e_l <= LSE_ABS, msg
+    assert_within_bound(o8, a["star"], a["bound"], what)
     return r_bf
+
+
+def _check(o8, l8, q, k, v, q8, k8, v8, eq, ek, sv, scale, rows=None, what=""):
+    """Gates and the elementwise P-rounding bound (x108 P, as attn_fwd_fp8);
+    rows None: every row, else [H, r] rows per head."""
+    q8n, k8n, v8n, eqn, ekn = (t.cpu().numpy() for t in (q8, k8, v8, eq, ek))
+    s_v = float(sv.item())
+    acc = {key: [] for key in ("o", "l", "bf", "dq", "ldq", "star", "bound")}
+    for hs, r in head_groups(rows, q.shape[1]):
+        o_dq, l_dq = oracle.attention_fp8_rows(q8n[:, hs], k8n[:, hs], v8n[:, hs], eqn[:, hs],
+                                               ekn[:, hs], s_v, scale, rows=r)
+        o_bf, _ = oracle.attention(q[:, hs].cpu(), k[:, hs].cpu(), v[:, hs].cpu(), scale, rows=r)
+        o_st, bd = fp8_p_rounding_bound(deq_rows(q8n[:, hs], eqn[:, hs]),
+                                        deq_rows(k8n[:, hs], ekn[:, hs]),
+                                        deq_per_tensor(v8n[:, hs], s_v), scale,
+                                        p_scale=KERNEL_P_SCALE, rows=r)
+        for key, val in (("o", to64(take_rows(o8, hs, r))), ("l", to64(take_rows(l8, hs, r))),
+                         ("bf", o_bf), ("dq", o_dq), ("ldq", l_dq), ("star", o_st),
+                         ("bound", bd)):
+            acc[key].append(val)
+    return _gates(acc, what)
 
 
 @pytest.mark.parametrize("B,H,Nq,Nkv,D", [(1, 2, 300, 300, 128), (1, 3, 200, 131, 64),
@@ -84,27 +102,29 @@ def test_attention_rows_shapes(B, H, Nq, Nkv, D):
     _check(o8, l8, q, k, v, q8, k8, v8, eq, ek, sv, D ** -0.5, what="fp8 rows")
 
 
-def test_attention_rows_flux_sampled():
+def test_attention_rows_flux_rows_per_head():
     c = workloads.CONFIGS["flux_1024_fp8"]
     print("CASE fp8 rows flux", flush=True)
     q, k, v = workloads.workload_qkv("flux_1024_fp8", device=DEV)
     q8, k8, v8, eq, ek, sv = _rows_path(q, k, v)
     o8, l8 = dta.attn_fwd_fp8_rows(q8, k8, v8, eq, ek, sv, c["D"] ** -0.5)
     torch.cuda.synchronize()
-    rows = workloads.sample_rows(c["config"], c["N"], 256, c["n_text"])
+    rows = workloads.sample_rows_per_head(c["config"], c["N"], c["H"], 256, c["n_text"])
     _check(o8, l8, q, k, v, q8, k8, v8, eq, ek, sv, c["D"] ** -0.5, rows=rows, what="fp8 rows flux")
 
 
 def _video_length_inputs():
     # Two heads of the HunyuanVideo 720p x 129-frame recipe at its full
-    # sequence length (119 056 tokens: 1861 K/V tiles, the last one 16 keys).
+    # sequence length (119 056 tokens: 1861 K/V tiles, the last one 16 keys),
+    # 256 rows per head (forced edge rows, one in each 32-row block dealt to
+    # the head).
     c = workloads.CONFIGS["hunyuan_720p_129f"]
     N, D = c["N"], c["D"]
     q, k, v = workloads.make_qkv(c["config"], 1, 2, N, N, D, device=DEV)
-    return q, k, v, D ** -0.5, workloads.sample_rows(c["config"], N, 256, c["n_text"])
+    return q, k, v, D ** -0.5, workloads.sample_rows_per_head(c["config"], N, 2, 256, c["n_text"])
 
 
-def test_attention_rows_video_length_sampled():
+def test_attention_rows_video_length_rows_per_head():
     print("CASE fp8 rows video length, 2 heads", flush=True)
     q, k, v, scale, rows = _video_length_inputs()
     q8, k8, v8, eq, ek, sv = _rows_path(q, k, v)
@@ -162,24 +182,27 @@ def _rows_v_path(q, k, v):
 
 
 def _check_v(o8, l8, q, k, v, q8, k8, v8, eq, ek, ev, scale, rows=None, what=""):
-    o_dq, l_dq = oracle.attention_fp8_rows_v(q8.cpu().numpy(), k8.cpu().numpy(), v8.cpu().numpy(),
-                                             eq.cpu().numpy(), ek.cpu().numpy(), ev.cpu().numpy(),
-                                             scale, rows=rows)
-    o_bf, _ = oracle.attention(q.cpu(), k.cpu(), v.cpu(), scale, rows=rows)
-    if rows is not None:
-        rt = torch.from_numpy(rows).to(o8.device)
-        o8, l8 = o8[:, :, rt], l8[:, :, rt]
-    o8, l8 = to64(o8), to64(l8)
-    assert np.isfinite(o8).all() and np.isfinite(l8).all()
-    mean_abs = np.abs(o8 - o_bf).mean()
-    r_bf, r_dq = rel_l2(o8, o_bf), rel_l2(o8, o_dq)
-    e_l = np.abs(l8 - l_dq).max()
-    msg = "%s: O mean-abs %.3e, rel-L2 %.3e (bf16) %.3e (dequant), LSE %.3e" % (
-        what, mean_abs, r_bf, r_dq, e_l)
-    print(msg)
-    assert mean_abs <= FP8_O_MEAN_ABS and r_bf <= FP8_REL_L2_VS_BF16, msg
-    assert r_dq <= FP8_REL_L2_VS_DEQUANT and e_l <= LSE_ABS, msg
-    return r_bf
+    """Gates against the oracle with one P scale per (query, 32 consecutive
+    keys) -- the block attn_fwd_fp8_rows_v documents -- and the per-block
+    elementwise bound; rows None: every row, else [H, r] rows per head."""
+    q8n, k8n, v8n, eqn, ekn, evn = (t.cpu().numpy() for t in (q8, k8, v8, eq, ek, ev))
+    acc = {key: [] for key in ("o", "l", "bf", "dq", "ldq", "star", "bound")}
+    for hs, r in head_groups(rows, q.shape[1]):
+        o_dq, l_dq = oracle.attention_fp8_rows_v(q8n[:, hs], k8n[:, hs], v8n[:, hs], eqn[:, hs],
+                                                 ekn[:, hs], evn[:, hs], scale,
+                                                 block=KERNEL_P_BLOCK, rows=r)
+        o_bf, _ = oracle.attention(q[:, hs].cpu(), k[:, hs].cpu(), v[:, hs].cpu(), scale, rows=r)
+        ev_h = evn[:, hs].astype(np.int64).reshape(v8n[:, hs].shape[:-1]) - 127
+        o_st, bd = fp8_p_rounding_bound(deq_rows(q8n[:, hs], eqn[:, hs]),
+                                        deq_rows(k8n[:, hs], ekn[:, hs]),
+                                        deq_rows(v8n[:, hs], evn[:, hs]), scale,
+                                        vq=oracle.e4m3_decode(v8n[:, hs]), ev=ev_h,
+                                        block=KERNEL_P_BLOCK, rows=r)
+        for key, val in (("o", to64(take_rows(o8, hs, r))), ("l", to64(take_rows(l8, hs, r))),
+                         ("bf", o_bf), ("dq", o_dq), ("ldq", l_dq), ("star", o_st),
+                         ("bound", bd)):
+            acc[key].append(val)
+    return _gates(acc, what)
 
 
 @pytest.mark.parametrize("B,H,Nq,Nkv,D", [(1, 2, 300, 300, 128), (1, 3, 200, 131, 64),
@@ -194,19 +217,19 @@ def test_attention_rows_v_shapes(B, H, Nq, Nkv, D):
     _check_v(o8, l8, q, k, v, q8, k8, v8, eq, ek, ev, D ** -0.5, what="fp8 rows_v")
 
 
-def test_attention_rows_v_flux_sampled():
+def test_attention_rows_v_flux_rows_per_head():
     c = workloads.CONFIGS["flux_1024_fp8"]
     print("CASE fp8 rows_v flux", flush=True)
     q, k, v = workloads.workload_qkv("flux_1024_fp8", device=DEV)
     q8, k8, v8, eq, ek, ev = _rows_v_path(q, k, v)
     o8, l8 = dta.attn_fwd_fp8_rows_v(q8, k8, v8, eq, ek, ev, c["D"] ** -0.5)
     torch.cuda.synchronize()
-    rows = workloads.sample_rows(c["config"], c["N"], 256, c["n_text"])
+    rows = workloads.sample_rows_per_head(c["config"], c["N"], c["H"], 256, c["n_text"])
     _check_v(o8, l8, q, k, v, q8, k8, v8, eq, ek, ev, c["D"] ** -0.5, rows=rows,
              what="fp8 rows_v flux")
 
 
-def test_attention_rows_v_video_length_sampled():
+def test_attention_rows_v_video_length_rows_per_head():
     print("CASE fp8 rows_v video length, 2 heads", flush=True)
     q, k, v, scale, rows = _video_length_inputs()
     q8, k8, v8, eq, ek, ev = _rows_v_path(q, k, v)

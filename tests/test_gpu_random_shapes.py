@@ -10,8 +10,10 @@ import torch
 import diffusion_transformer_attention_flash_amd as dta
 import oracle
 import workloads
-from helpers import (FP8_O_MEAN_ABS, FP8_REL_L2_VS_BF16, FP8_REL_L2_VS_DEQUANT, LSE_ABS,
-                     assert_bf16_attention, rel_l2, to64)
+from helpers import (FP8_O_MEAN_ABS, FP8_REL_L2_VS_BF16, FP8_REL_L2_VS_DEQUANT,
+                     KERNEL_P_BLOCK, KERNEL_P_SCALE, LSE_ABS, assert_bf16_attention,
+                     assert_within_bound, deq_per_tensor, deq_rows, fp8_p_rounding_bound,
+                     rel_l2, to64)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -90,6 +92,10 @@ def test_random_shape_fp8_variants(i):
     o_dq, l_dq = oracle.attention_fp8(q8.cpu().numpy(), k8.cpu().numpy(), v8.cpu().numpy(),
                                       ds.cpu().tolist(), scale)
     _gates(o8, l8, o_bf, o_dq, l_dq, "random fp8 per-tensor")
+    dsc = ds.cpu().tolist()
+    o_st, bd = fp8_p_rounding_bound(deq_per_tensor(q8, dsc[0]), deq_per_tensor(k8, dsc[1]),
+                                    deq_per_tensor(v8, dsc[2]), scale, p_scale=KERNEL_P_SCALE)
+    assert_within_bound(o8, o_st, bd, "random fp8 per-tensor")
     # row-wise Q/K
     rq8, eq = dta.fp8_quant_rows_pow2(q)
     rk8, ek = dta.fp8_quant_rows_pow2(k)
@@ -99,11 +105,21 @@ def test_random_shape_fp8_variants(i):
                                            eq.cpu().numpy(), ek.cpu().numpy(), float(sv.item()),
                                            scale)
     _gates(o8, l8, o_bf, o_dq, l_dq, "random fp8 rows")
+    o_st, bd = fp8_p_rounding_bound(deq_rows(rq8, eq), deq_rows(rk8, ek),
+                                    deq_per_tensor(v8, float(sv.item())), scale,
+                                    p_scale=KERNEL_P_SCALE)
+    assert_within_bound(o8, o_st, bd, "random fp8 rows")
     # row-wise Q/K/V with per-block P scales
     rv8, ev = dta.fp8_quant_rows_pow2(v)
     o8, l8 = dta.attn_fwd_fp8_rows_v(rq8, rk8, rv8, eq, ek, ev, scale)
     torch.cuda.synchronize()
     o_dq, l_dq = oracle.attention_fp8_rows_v(rq8.cpu().numpy(), rk8.cpu().numpy(),
                                              rv8.cpu().numpy(), eq.cpu().numpy(),
-                                             ek.cpu().numpy(), ev.cpu().numpy(), scale)
+                                             ek.cpu().numpy(), ev.cpu().numpy(), scale,
+                                             block=KERNEL_P_BLOCK)
     _gates(o8, l8, o_bf, o_dq, l_dq, "random fp8 rows_v")
+    ev_i = ev.cpu().numpy().astype(np.int64).reshape(B, H, Nkv) - 127
+    o_st, bd = fp8_p_rounding_bound(deq_rows(rq8, eq), deq_rows(rk8, ek), deq_rows(rv8, ev), scale,
+                                    vq=oracle.e4m3_decode(rv8.cpu().numpy()), ev=ev_i,
+                                    block=KERNEL_P_BLOCK)
+    assert_within_bound(o8, o_st, bd, "random fp8 rows_v")

@@ -325,6 +325,32 @@ def test_z13_encode_matches_torch_in_range():
     np.testing.assert_array_equal(mine, ref)
 
 
+def test_z13_round_equals_encode_then_decode():
+    """e4m3_round (spacing arithmetic) against e4m3_encode + e4m3_decode (the
+    code table) and torch's float8_e4m3fn cast, over every code, every
+    midpoint, points just off the midpoints, both subnormal and normal
+    ranges, saturation, signed zeros and NaN."""
+    mags = oracle.e4m3_decode(np.arange(0x7F, dtype=np.uint8))
+    mids = 0.5 * (mags[:-1] + mags[1:])
+    eps = np.nextafter(mids, np.inf) - mids
+    x = np.concatenate([
+        mags, -mags, mids, -mids, mids + eps, mids - eps,
+        RNG.standard_normal(20000) * 40, RNG.uniform(-2 ** -5, 2 ** -5, 5000),
+        np.exp2(RNG.uniform(-14, 9, 5000)),
+        [448.0, 463.99, 464.0, 470.0, 1e30, -1e30, np.inf, -np.inf, 0.0, -0.0,
+         2 ** -10, 2 ** -10 * (1 + 1e-12), 3 * 2 ** -10],
+    ])
+    r = oracle.e4m3_round(x)
+    ref = oracle.e4m3_decode(oracle.e4m3_encode(x))
+    assert np.array_equal(r, ref)
+    assert np.array_equal(np.signbit(r), np.signbit(ref))
+    assert np.isnan(oracle.e4m3_round(np.array([np.nan])))[0]
+    fin = np.abs(x) < 448                        # torch's cast saturates only in range
+    t = torch.from_numpy(x[fin].astype(np.float32)).to(torch.float8_e4m3fn).to(torch.float64)
+    x32 = x[fin].astype(np.float32).astype(np.float64)
+    assert np.array_equal(oracle.e4m3_round(x32), t.numpy())
+
+
 def test_z13_encode_saturates():
     x = np.array([448.0, 463.9, 464.0, 500.0, 1e30, -1e30, np.nan])
     assert list(oracle.e4m3_encode(x)) == [0x7E, 0x7E, 0x7E, 0x7E, 0x7E, 0xFE, 0x7F]
@@ -627,14 +653,18 @@ def test_rows_pow2_attention_beats_per_tensor_on_outlier_tokens():
 
 # ---- per-token V and per-block P scales (attention_fp8_rows_v) ----
 
-def test_p_block_partition():
+@pytest.mark.parametrize("block", [1, 7, 32, 64])
+def test_p_block_partition(block):
     for nkv in (1, 5, 32, 33, 64, 100, 4608):
-        blk = oracle.p_block_ids(nkv)
+        blk = oracle.p_block_ids(nkv, block)
         assert blk.shape == (nkv,) and blk[0] == 0
-        n_blocks = -(-nkv // 32)
+        n_blocks = -(-nkv // block)
         assert blk.max() == n_blocks - 1
-        for b in range(n_blocks):                  # 32 consecutive keys, a short last block
-            assert np.array_equal(np.nonzero(blk == b)[0], np.arange(32 * b, min(32 * b + 32, nkv)))
+        for b in range(n_blocks):                  # consecutive keys, a short last block
+            assert np.array_equal(np.nonzero(blk == b)[0],
+                                  np.arange(block * b, min(block * b + block, nkv)))
+    with pytest.raises(ValueError):
+        oracle.p_block_ids(10, 0)
 
 
 def test_p_block_exponent_is_minimal_and_codes_match_torch():
@@ -645,7 +675,7 @@ def test_p_block_exponent_is_minimal_and_codes_match_torch():
           * np.exp2(rng.integers(-40, 20, size=(7, 1)).astype(np.float64)))
     pv[3, :] = 0.0
     pv[4, 64:128] = 0.0
-    blk = oracle.p_block_ids(n)
+    blk = oracle.p_block_ids(n, 32)
     codes, e = oracle.quant_p_blocks(pv, blk)
     for r in range(pv.shape[0]):
         for b in range(e.shape[1]):
@@ -674,7 +704,7 @@ def test_rows_v_uniform_scores_give_the_mean_of_v():
     kr, ek = oracle.quant_rows_pow2(k, D)
     vr, ev = oracle.quant_rows_pow2(v, D)
     o, lse = oracle.attention_fp8_rows_v(qr, kr, vr, eq.reshape(B, H, N), ek.reshape(B, H, N),
-                                         ev.reshape(B, H, N), 0.125)
+                                         ev.reshape(B, H, N), 0.125, block=32)
     v_deq = oracle.e4m3_decode(vr) * np.exp2(ev.reshape(B, H, N, 1).astype(np.float64) - 127)
     mean = v_deq.mean(axis=2, keepdims=True)
     assert np.allclose(o, np.broadcast_to(mean, o.shape), rtol=1e-12, atol=1e-12)
@@ -702,7 +732,7 @@ def test_rows_v_beats_per_tensor_v_on_an_outlier_value_token():
     sh = (B, H, N)
     o_t, _ = oracle.attention_fp8_rows(qr, kr, vt, eq.reshape(sh), ek.reshape(sh), sv, scale)
     o_v, _ = oracle.attention_fp8_rows_v(qr, kr, vr, eq.reshape(sh), ek.reshape(sh),
-                                         ev.reshape(sh), scale)
+                                         ev.reshape(sh), scale, block=32)
     d = slice(8, None)
     ref = np.linalg.norm(o_ref[..., d])
     err_t = np.linalg.norm((o_t - o_ref)[..., d]) / ref
@@ -736,8 +766,71 @@ def test_rows_v_keeps_a_diffuse_tail_that_x448_p_scaling_flushes():
     o_ref, _ = oracle.attention(*deq, scale)
     o_t, _ = oracle.attention_fp8_rows(qr, kr, vt, eq.reshape(1, 1, 1), ek.reshape(1, 1, N), sv, scale)
     o_v, _ = oracle.attention_fp8_rows_v(qr, kr, vr, eq.reshape(1, 1, 1), ek.reshape(1, 1, N),
-                                         ev.reshape(1, 1, N), scale)
+                                         ev.reshape(1, 1, N), scale, block=32)
     ref = np.linalg.norm(o_ref)
     err_t = np.linalg.norm(o_t - o_ref) / ref
     err_v = np.linalg.norm(o_v - o_ref) / ref
     assert err_t > 0.9 and err_v < 0.1, (err_v, err_t)
+
+
+def _rows_v_inputs(v_vals, v_exps, k_vals=None, d=1):
+    """One head, one query (Q = 1 in dim 0), keys K[j, 0] = k_vals[j] (0 if
+    None), V[j, :] = v_vals[j] with per-token exponents v_exps[j]; all codes
+    exact E4M3 values with exponent bytes 127 for Q and K."""
+    n = len(v_vals)
+    q8 = oracle.e4m3_encode(np.ones((1, 1, 1, d)))
+    kv = np.zeros((1, 1, n, d))
+    if k_vals is not None:
+        kv[0, 0, :, 0] = k_vals
+    k8 = oracle.e4m3_encode(kv)
+    v8 = oracle.e4m3_encode(np.repeat(np.asarray(v_vals, dtype=np.float64)[:, None], d, 1)
+                            .reshape(1, 1, n, d))
+    assert np.array_equal(oracle.e4m3_decode(k8), kv)
+    eq = np.full((1, 1, 1), 127, dtype=np.uint8)
+    ek = np.full((1, 1, n), 127, dtype=np.uint8)
+    ev = (np.asarray(v_exps, dtype=np.int64) + 127).astype(np.uint8).reshape(1, 1, n)
+    return q8, k8, v8, eq, ek, ev
+
+
+def test_rows_v_block_size_closed_form_uniform_scores():
+    """Scale 0: every p is 1, so pv_j = 2^ev_j and each block's scale is
+    2^(max ev - 8). A key survives iff 2^(ev_j - max ev + 8) is at least the
+    smallest E4M3 subnormal 2^-9 (2^-10 ties to 0), i.e. ev_j >= max ev - 17
+    over its block; survivors are exact. O = sum of surviving V / N, which
+    tells the block sizes apart: key 10 is large, keys 20 and 40 are 2^-20 of
+    it; key 20 shares a 32-block with key 10, key 40 only a 64-block."""
+    n = 128
+    vals = 1.0 + (np.arange(n) % 7) / 8.0                 # exact E4M3 values
+    ex = np.zeros(n, dtype=np.int64)
+    ex[10] = 12
+    ex[20] = ex[40] = -8
+    q8, k8, v8, eq, ek, ev = _rows_v_inputs(vals, ex)
+    v = vals * np.exp2(ex)
+    for block, dropped in ((1, []), (32, [20]), (64, [20, 40]), (128, [20, 40]), (1000, [20, 40])):
+        o, lse = oracle.attention_fp8_rows_v(q8, k8, v8, eq, ek, ev, 0.0, block=block)
+        keep = np.ones(n, bool)
+        keep[dropped] = False
+        assert o[0, 0, 0, 0] == pytest.approx(v[keep].sum() / n, rel=1e-14), block
+        assert lse[0, 0, 0] == pytest.approx(math.log(n), rel=1e-14)
+
+
+@pytest.mark.parametrize("block", [1, 64])
+def test_rows_v_exact_power_of_two_probabilities(block):
+    """Scores -k ln2 (Q = 1, K = -k, scale ln 2): p_j is 2^-k_j to within
+    float64 rounding, so pv_j = 2^(ev_j - k_j) rounds to that power of two
+    exactly whenever it is within 2^17 of its block's largest. O = sum_j
+    2^-k_j v_j / sum_j 2^-k_j over the survivors, LSE = ln sum_j 2^-k_j."""
+    kk = np.array([0, 1, 2, 3, 1, 0, 2, 5, 4, 3] * 7, dtype=np.float64)   # 70 keys
+    n = kk.size
+    vals = np.array([1.0, -2.0, 3.0, 0.5, 1.5, -1.0, 2.5] * 10)
+    ex = np.array([0, 2, -3, 1, 0, 0, 4, -1, 2, 0] * 7, dtype=np.int64)
+    ex[65] = -30                                          # 2^-30 * 2^-0: far below its block
+    q8, k8, v8, eq, ek, ev = _rows_v_inputs(vals, ex, k_vals=-kk)
+    o, lse = oracle.attention_fp8_rows_v(q8, k8, v8, eq, ek, ev, math.log(2.0), block=block)
+    p = np.exp2(-kk)
+    keep = np.ones(n, bool)
+    if block == 64:
+        keep[65] = False                                  # shares block 1 (keys 64..69) with 2^4
+    num = (p * vals * np.exp2(ex))[keep].sum()
+    assert o[0, 0, 0, 0] == pytest.approx(num / p.sum(), rel=1e-13)
+    assert lse[0, 0, 0] == pytest.approx(math.log(p.sum()), rel=1e-13)

@@ -126,6 +126,43 @@ def sample_rows(config, n, count=256, n_text=0, tile=64):
     return np.sort(np.concatenate([np.asarray(forced), drawn]).astype(np.int64))
 
 
+def sample_rows_per_head(config, n, heads, count=256, n_text=0, block=32, tile=64):
+    """Seeded query rows for each head: an int64 array [heads, count], each
+    head's rows sorted and distinct.
+
+    Every head gets the forced edge rows of ``sample_rows``. The ``block``-row
+    blocks of the sequence are dealt round-robin to the heads (block b to
+    head b % heads) and each head draws one row inside each of its blocks, so
+    that across the heads every block of ``block`` consecutive query rows is
+    compared at least once when ``count`` leaves room for it (otherwise a
+    seeded subset of the head's blocks); the remaining rows are drawn
+    uniformly from the rest. One random stream per head, seeded by the
+    config's rows slot and the head index.
+    """
+    count = min(int(count), int(n))
+    forced = [0, n - 1]
+    if 0 < n_text < n:
+        forced += [n_text - 1, n_text]
+    forced.append(n - (n % tile) if n % tile else max(n - tile, 0))
+    forced = sorted(set(int(r) for r in forced if 0 <= r < n))[:count]
+    n_blocks = -(-int(n) // block)
+    out = np.empty((heads, count), dtype=np.int64)
+    for h in range(heads):
+        rng = np.random.default_rng([seed_of(config, SLOT_ROWS), h])
+        mine = np.arange(h, n_blocks, heads)
+        room = count - len(forced)
+        if mine.size > room:
+            mine = np.sort(rng.choice(mine, size=room, replace=False))
+        lo = mine * block
+        hi = np.minimum(lo + block, n)
+        picked = lo + (rng.random(mine.size) * (hi - lo)).astype(np.int64)
+        chosen = np.union1d(np.asarray(forced, dtype=np.int64), picked)
+        pool = np.setdiff1d(np.arange(n), chosen)
+        extra = rng.choice(pool, size=count - chosen.size, replace=False)
+        out[h] = np.sort(np.concatenate([chosen, extra]))
+    return out
+
+
 def residual_pair(config, shape, noise=0.08, device="cpu"):
     """b ~ N(0,1) -> bf16; a = bf16(float(b) + noise * N(0,1))."""
     b = _normal(shape, seed_of(config, SLOT_RES), device).to(torch.bfloat16)
