@@ -44,16 +44,43 @@ def _stream(t):
 
 
 def _need(t, name, dtype, ndim=None):
+    """Type, dtype, rank and contiguity of one tensor argument (the device is
+    checked once for all arguments by _gpu)."""
     if not isinstance(t, torch.Tensor):
         raise TypeError("%s must be a torch.Tensor" % name)
-    if t.device.type != "cuda":
-        raise ValueError("%s must be on a GPU, got %s" % (name, t.device))
     if t.dtype != dtype:
         raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
     if ndim is not None and t.dim() != ndim:
         raise ValueError("%s must have %d dims, got shape %s" % (name, ndim, tuple(t.shape)))
     if not t.is_contiguous():
         raise ValueError("%s must be contiguous" % name)
+
+
+def _out(t, name, dtype, shape):
+    """A caller-supplied output (None: the binding allocates it): dtype,
+    contiguity and the exact shape (a tuple) or element count (an int)."""
+    if t is None:
+        return
+    _need(t, name, dtype)
+    if isinstance(shape, int):
+        if t.numel() != shape:
+            raise ValueError("%s must hold %d elements, got shape %s" % (name, shape, tuple(t.shape)))
+    elif tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+
+
+def _gpu(**named):
+    """Every given tensor on one GPU (None entries are skipped)."""
+    dev = None
+    for name, t in named.items():
+        if t is None:
+            continue
+        if t.device.type != "cuda":
+            raise ValueError("%s must be on a GPU, got %s" % (name, t.device))
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("%s is on %s, the other tensors on %s" % (name, t.device, dev))
 
 
 def _ptr(t):
@@ -88,20 +115,15 @@ def attn_fwd(q, k, v, scale=None, o=None, lse=None):
     Nkv = k.shape[2]
     if tuple(k.shape) != (B, H, Nkv, D) or tuple(v.shape) != (B, H, Nkv, D):
         raise ValueError("shape mismatch: q %s k %s v %s" % (tuple(q.shape), tuple(k.shape), tuple(v.shape)))
+    _out(o, "o", torch.bfloat16, (B, H, Nq, D))
+    _out(lse, "lse", torch.float32, (B, H, Nq))
+    _gpu(q=q, k=k, v=v, o=o, lse=lse)
     if scale is None:
         scale = D ** -0.5
     if o is None:
         o = torch.empty_like(q)
-    else:
-        _need(o, "o", torch.bfloat16, 4)
-        if o.shape != q.shape:
-            raise ValueError("o must have q's shape")
     if lse is None:
         lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
-    else:
-        _need(lse, "lse", torch.float32, 3)
-        if tuple(lse.shape) != (B, H, Nq):
-            raise ValueError("lse must be [B,H,Nq]")
     st = _lib.lib().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
                              B, H, Nq, Nkv, D, float(scale), ctypes_ptr(_stream(q)))
     _lib.check("attn_fwd", st)
@@ -115,14 +137,13 @@ def attn_merge(o_parts, lse_parts, o=None, lse=None):
     n, B, H, Nq, D = o_parts.shape
     if tuple(lse_parts.shape) != (n, B, H, Nq):
         raise ValueError("lse_parts must be [n,B,H,Nq]")
+    _out(o, "o", torch.bfloat16, (B, H, Nq, D))
+    _out(lse, "lse", torch.float32, (B, H, Nq))
+    _gpu(o_parts=o_parts, lse_parts=lse_parts, o=o, lse=lse)
     if o is None:
         o = torch.empty((B, H, Nq, D), dtype=torch.bfloat16, device=o_parts.device)
-    else:
-        _need(o, "o", torch.bfloat16, 4)
     if lse is None:
         lse = torch.empty((B, H, Nq), dtype=torch.float32, device=o_parts.device)
-    else:
-        _need(lse, "lse", torch.float32, 3)
     st = _lib.lib().attn_merge(_ptr(o_parts), _ptr(lse_parts), n, _ptr(o), _ptr(lse),
                                B, H, Nq, D, ctypes_ptr(_stream(o_parts)))
     _lib.check("attn_merge", st)
@@ -135,14 +156,15 @@ def attn_fwd_accum(q, k, v, o, lse, scale=None):
     _need(q, "q", torch.bfloat16, 4)
     _need(k, "k", torch.bfloat16, 4)
     _need(v, "v", torch.bfloat16, 4)
-    _need(o, "o", torch.bfloat16, 4)
-    _need(lse, "lse", torch.float32, 3)
     B, H, Nq, D = q.shape
     Nkv = k.shape[2]
     if tuple(k.shape) != (B, H, Nkv, D) or tuple(v.shape) != (B, H, Nkv, D):
         raise ValueError("shape mismatch: q %s k %s v %s" % (tuple(q.shape), tuple(k.shape), tuple(v.shape)))
-    if o.shape != q.shape or tuple(lse.shape) != (B, H, Nq):
-        raise ValueError("o must have q's shape and lse must be [B,H,Nq]")
+    if o is None or lse is None:
+        raise ValueError("attn_fwd_accum needs the running o and lse")
+    _out(o, "o", torch.bfloat16, (B, H, Nq, D))
+    _out(lse, "lse", torch.float32, (B, H, Nq))
+    _gpu(q=q, k=k, v=v, o=o, lse=lse)
     if scale is None:
         scale = D ** -0.5
     st = _lib.lib().attn_fwd_accum(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
@@ -154,12 +176,13 @@ def attn_fwd_accum(q, k, v, o, lse, scale=None):
 def attn_merge_into(o, lse, o_part, lse_part):
     """(o, lse) <- merge((o, lse), (o_part, lse_part)) in place; returns (o, lse)."""
     _need(o, "o", torch.bfloat16, 4)
-    _need(lse, "lse", torch.float32, 3)
-    _need(o_part, "o_part", torch.bfloat16, 4)
-    _need(lse_part, "lse_part", torch.float32, 3)
     B, H, Nq, D = o.shape
-    if o_part.shape != o.shape or lse.shape != lse_part.shape or tuple(lse.shape) != (B, H, Nq):
-        raise ValueError("o/o_part must match and lse/lse_part must be [B,H,Nq]")
+    _out(lse, "lse", torch.float32, (B, H, Nq))
+    _out(o_part, "o_part", torch.bfloat16, (B, H, Nq, D))
+    _out(lse_part, "lse_part", torch.float32, (B, H, Nq))
+    if lse is None or o_part is None or lse_part is None:
+        raise ValueError("attn_merge_into needs o, lse, o_part and lse_part")
+    _gpu(o=o, lse=lse, o_part=o_part, lse_part=lse_part)
     st = _lib.lib().attn_merge_into(_ptr(o), _ptr(lse), _ptr(o_part), _ptr(lse_part),
                                     B, H, Nq, D, ctypes_ptr(_stream(o)))
     _lib.check("attn_merge_into", st)
@@ -172,10 +195,10 @@ def residual_diff(a, b, out=None):
     _need(b, "b", torch.bfloat16)
     if a.numel() != b.numel():
         raise ValueError("a and b must have the same number of elements")
+    _out(out, "out", torch.float32, 1)
+    _gpu(a=a, b=b, out=out)
     if out is None:
         out = torch.empty((), dtype=torch.float32, device=a.device)
-    else:
-        _need(out, "out", torch.float32)
     ws = workspace(a.device)
     st = _lib.lib().residual_diff(_ptr(a), _ptr(b), a.numel(), _ptr(out), _ptr(ws),
                                   ctypes_ptr(_stream(a)))
@@ -195,6 +218,9 @@ def fbcache_step(r, r_prev, threshold, hidden, cached, diff=None, use_cache=None
         raise ValueError("r and r_prev must have the same number of elements")
     if hidden.numel() != cached.numel():
         raise ValueError("hidden and cached must have the same number of elements")
+    _out(diff, "diff", torch.float32, 1)
+    _out(use_cache, "use_cache", torch.int32, 1)
+    _gpu(r=r, r_prev=r_prev, hidden=hidden, cached=cached, diff=diff, use_cache=use_cache)
     if diff is None:
         diff = torch.empty((), dtype=torch.float32, device=r.device)
     if use_cache is None:
@@ -208,7 +234,6 @@ def fbcache_step(r, r_prev, threshold, hidden, cached, diff=None, use_cache=None
 
 
 def _host_ints(vals, name):
-    import ctypes
     vals = [int(x) for x in vals]
     if not vals:
         raise ValueError("%s must not be empty" % name)
@@ -216,8 +241,8 @@ def _host_ints(vals, name):
 
 
 def _layout_check(t, name, numel):
-    if not isinstance(t, torch.Tensor) or not t.is_cuda:
-        raise ValueError("%s must be a CUDA tensor" % name)
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
     if t.element_size() != 2 or not t.is_contiguous():
         raise ValueError("%s must be a contiguous 16-bit tensor" % name)
     if t.numel() != numel:
@@ -229,9 +254,11 @@ def seq_concat(parts, lens, B, H, D, padded=None, out=None):
     with lens[p] valid tokens) into out [B,H,sum(lens),D]."""
     pads = list(lens) if padded is None else list(padded)
     _layout_check(parts, "parts", B * H * sum(pads) * D)
+    if out is not None:
+        _layout_check(out, "out", B * H * sum(lens) * D)
+    _gpu(parts=parts, out=out)
     if out is None:
         out = torch.empty((B, H, sum(lens), D), dtype=parts.dtype, device=parts.device)
-    _layout_check(out, "out", B * H * sum(lens) * D)
     cl, n = _host_ints(lens, "lens")
     cp, _ = _host_ints(pads, "padded")
     st = _lib.lib().seq_concat(_ptr(parts), _ptr(out), n, cl, cp, B, H, D,
@@ -246,9 +273,11 @@ def seq_split(x, lens, padded=None, parts=None):
     B, H, S, D = x.shape
     pads = list(lens) if padded is None else list(padded)
     _layout_check(x, "x", B * H * sum(lens) * D)
+    if parts is not None:
+        _layout_check(parts, "parts", B * H * sum(pads) * D)
+    _gpu(x=x, parts=parts)
     if parts is None:
         parts = torch.empty(B * H * sum(pads) * D, dtype=x.dtype, device=x.device)
-    _layout_check(parts, "parts", B * H * sum(pads) * D)
     cl, n = _host_ints(lens, "lens")
     cp, _ = _host_ints(pads, "padded")
     st = _lib.lib().seq_split(_ptr(x), _ptr(parts), n, cl, cp, B, H, D, ctypes_ptr(_stream(x)))
@@ -260,9 +289,11 @@ def head_concat(parts, heads, B, N, D, out=None):
     """Concatenate P head-parts (packed, part p = [B,heads[p],N,D]) into
     out [B,sum(heads),N,D]."""
     _layout_check(parts, "parts", B * sum(heads) * N * D)
+    if out is not None:
+        _layout_check(out, "out", B * sum(heads) * N * D)
+    _gpu(parts=parts, out=out)
     if out is None:
         out = torch.empty((B, sum(heads), N, D), dtype=parts.dtype, device=parts.device)
-    _layout_check(out, "out", B * sum(heads) * N * D)
     ch, n = _host_ints(heads, "heads")
     st = _lib.lib().head_concat(_ptr(parts), _ptr(out), n, ch, B, N, D, ctypes_ptr(_stream(parts)))
     _lib.check("head_concat", st)
@@ -274,9 +305,11 @@ def head_split(x, heads, parts=None):
     returns the flat packed buffer."""
     B, Hs, N, D = x.shape
     _layout_check(x, "x", B * sum(heads) * N * D)
+    if parts is not None:
+        _layout_check(parts, "parts", x.numel())
+    _gpu(x=x, parts=parts)
     if parts is None:
         parts = torch.empty(x.numel(), dtype=x.dtype, device=x.device)
-    _layout_check(parts, "parts", x.numel())
     ch, n = _host_ints(heads, "heads")
     st = _lib.lib().head_split(_ptr(x), _ptr(parts), n, ch, B, N, D, ctypes_ptr(_stream(x)))
     _lib.check("head_split", st)
@@ -286,16 +319,13 @@ def head_split(x, heads, parts=None):
 def fp8_quant_per_tensor(x, x8=None, descale=None):
     """Per-tensor E4M3FN quantisation of bf16 x -> (x8 uint8 codes, descale f32[1])."""
     _need(x, "x", torch.bfloat16)
+    _out(x8, "x8", torch.uint8, x.numel())
+    _out(descale, "descale", torch.float32, 1)
+    _gpu(x=x, x8=x8, descale=descale)
     if x8 is None:
         x8 = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
-    else:
-        _need(x8, "x8", torch.uint8)
-        if x8.numel() != x.numel():
-            raise ValueError("x8 must have x's element count")
     if descale is None:
         descale = torch.empty((1,), dtype=torch.float32, device=x.device)
-    else:
-        _need(descale, "descale", torch.float32)
     ws = workspace(x.device)
     st = _lib.lib().fp8_quant_per_tensor(_ptr(x), x.numel(), _ptr(x8), _ptr(descale),
                                          _ptr(ws), ctypes_ptr(_stream(x)))
@@ -310,27 +340,23 @@ def fp8_quant_per_tensor_multi(xs, x8s=None, descale=None):
     xs = list(xs)
     if not 1 <= len(xs) <= 4:
         raise ValueError("fp8_quant_per_tensor_multi takes 1 to 4 tensors")
-    dev = xs[0].device
     for i, x in enumerate(xs):
         _need(x, "xs[%d]" % i, torch.bfloat16)
-        if x.device != dev:
-            raise ValueError("all tensors must be on one device")
-    if x8s is None:
-        x8s = [torch.empty(x.shape, dtype=torch.uint8, device=dev) for x in xs]
-    else:
+    if x8s is not None:
         x8s = list(x8s)
         if len(x8s) != len(xs):
             raise ValueError("x8s must match xs")
         for i, (x, x8) in enumerate(zip(xs, x8s)):
-            _need(x8, "x8s[%d]" % i, torch.uint8)
-            if x8.numel() != x.numel():
-                raise ValueError("x8s[%d] must have xs[%d]'s element count" % (i, i))
+            _out(x8, "x8s[%d]" % i, torch.uint8, x.numel())
+    _out(descale, "descale", torch.float32, len(xs))
+    named = {"xs[%d]" % i: x for i, x in enumerate(xs)}
+    named.update({"x8s[%d]" % i: t for i, t in enumerate(x8s or [])})
+    _gpu(descale=descale, **named)
+    dev = xs[0].device
+    if x8s is None:
+        x8s = [torch.empty(x.shape, dtype=torch.uint8, device=dev) for x in xs]
     if descale is None:
         descale = torch.empty((len(xs),), dtype=torch.float32, device=dev)
-    else:
-        _need(descale, "descale", torch.float32)
-        if descale.numel() < len(xs):
-            raise ValueError("descale needs one float per tensor")
     n = len(xs)
     xp = (ctypes.c_void_p * n)(*[x.data_ptr() for x in xs])
     x8p = (ctypes.c_void_p * n)(*[t.data_ptr() for t in x8s])
@@ -344,24 +370,38 @@ def fp8_quant_per_tensor_multi(xs, x8s=None, descale=None):
     return x8s, descale
 
 
-def attn_fwd_fp8(q8, k8, v8, descale, scale=None, o=None, lse=None):
-    """fp8 attention: E4M3FN codes (uint8) q8/k8/v8, descale f32[3] = (s_q, s_k, s_v)."""
+def _fp8_qkv(q8, k8, v8):
     _need(q8, "q8", torch.uint8, 4)
     _need(k8, "k8", torch.uint8, 4)
     _need(v8, "v8", torch.uint8, 4)
-    _need(descale, "descale", torch.float32)
-    if descale.numel() != 3:
-        raise ValueError("descale must hold 3 floats (s_q, s_k, s_v)")
     B, H, Nq, D = q8.shape
     Nkv = k8.shape[2]
     if tuple(k8.shape) != (B, H, Nkv, D) or tuple(v8.shape) != (B, H, Nkv, D):
-        raise ValueError("shape mismatch")
+        raise ValueError("shape mismatch: q8 %s k8 %s v8 %s"
+                         % (tuple(q8.shape), tuple(k8.shape), tuple(v8.shape)))
+    return B, H, Nq, Nkv, D
+
+
+def _attn_outputs(o, lse, B, H, Nq, D, device):
+    if o is None:
+        o = torch.empty((B, H, Nq, D), dtype=torch.bfloat16, device=device)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=device)
+    return o, lse
+
+
+def attn_fwd_fp8(q8, k8, v8, descale, scale=None, o=None, lse=None):
+    """fp8 attention: E4M3FN codes (uint8) q8/k8/v8, descale f32[3] = (s_q, s_k, s_v)."""
+    B, H, Nq, Nkv, D = _fp8_qkv(q8, k8, v8)
+    _out(descale, "descale", torch.float32, 3)
+    if descale is None:
+        raise ValueError("descale must hold 3 floats (s_q, s_k, s_v)")
+    _out(o, "o", torch.bfloat16, (B, H, Nq, D))
+    _out(lse, "lse", torch.float32, (B, H, Nq))
+    _gpu(q8=q8, k8=k8, v8=v8, descale=descale, o=o, lse=lse)
     if scale is None:
         scale = D ** -0.5
-    if o is None:
-        o = torch.empty((B, H, Nq, D), dtype=torch.bfloat16, device=q8.device)
-    if lse is None:
-        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q8.device)
+    o, lse = _attn_outputs(o, lse, B, H, Nq, D, q8.device)
     st = _lib.lib().attn_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(descale), _ptr(o),
                                  _ptr(lse), B, H, Nq, Nkv, D, float(scale),
                                  ctypes_ptr(_stream(q8)))
@@ -376,18 +416,17 @@ def fp8_quant_rows_pow2(x, row_len=None, x8=None, e8m0=None):
     _need(x, "x", torch.bfloat16)
     if row_len is None:
         row_len = x.shape[-1]
-    if x.numel() % row_len:
+    if row_len < 1 or x.numel() % row_len:
         raise ValueError("row_len must divide the element count")
     rows = x.numel() // row_len
+    _out(x8, "x8", torch.uint8, x.numel())
+    _out(e8m0, "e8m0", torch.uint8, rows)
+    _gpu(x=x, x8=x8, e8m0=e8m0)
     if x8 is None:
         x8 = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
     if e8m0 is None:
         e8m0 = torch.empty(x.shape[:-1] if row_len == x.shape[-1] else (rows,),
                            dtype=torch.uint8, device=x.device)
-    _need(x8, "x8", torch.uint8)
-    _need(e8m0, "e8m0", torch.uint8)
-    if x8.numel() != x.numel() or e8m0.numel() != rows:
-        raise ValueError("x8 / e8m0 sizes do not match")
     st = _lib.lib().fp8_quant_rows_pow2(_ptr(x), rows, int(row_len), _ptr(x8), _ptr(e8m0),
                                         ctypes_ptr(_stream(x)))
     _lib.check("fp8_quant_rows_pow2", st)
@@ -397,24 +436,20 @@ def fp8_quant_rows_pow2(x, row_len=None, x8=None, e8m0=None):
 def attn_fwd_fp8_rows(q8, k8, v8, q_e8m0, k_e8m0, v_descale, scale=None, o=None, lse=None):
     """fp8 attention with per-token power-of-two Q/K scales (E8M0 bytes
     [B,H,N]) and V's per-tensor scale (f32[1])."""
-    _need(q8, "q8", torch.uint8, 4)
-    _need(k8, "k8", torch.uint8, 4)
-    _need(v8, "v8", torch.uint8, 4)
-    _need(q_e8m0, "q_e8m0", torch.uint8)
-    _need(k_e8m0, "k_e8m0", torch.uint8)
-    _need(v_descale, "v_descale", torch.float32)
-    B, H, Nq, D = q8.shape
-    Nkv = k8.shape[2]
-    if tuple(k8.shape) != (B, H, Nkv, D) or tuple(v8.shape) != (B, H, Nkv, D):
-        raise ValueError("shape mismatch")
-    if q_e8m0.numel() != B * H * Nq or k_e8m0.numel() != B * H * Nkv:
-        raise ValueError("q_e8m0 / k_e8m0 must hold one byte per token of each head")
+    B, H, Nq, Nkv, D = _fp8_qkv(q8, k8, v8)
+    for t, name, n in ((q_e8m0, "q_e8m0", B * H * Nq), (k_e8m0, "k_e8m0", B * H * Nkv)):
+        if t is None:
+            raise ValueError("%s is required" % name)
+        _out(t, name, torch.uint8, n)
+    if v_descale is None:
+        raise ValueError("v_descale is required")
+    _out(v_descale, "v_descale", torch.float32, 1)
+    _out(o, "o", torch.bfloat16, (B, H, Nq, D))
+    _out(lse, "lse", torch.float32, (B, H, Nq))
+    _gpu(q8=q8, k8=k8, v8=v8, q_e8m0=q_e8m0, k_e8m0=k_e8m0, v_descale=v_descale, o=o, lse=lse)
     if scale is None:
         scale = D ** -0.5
-    if o is None:
-        o = torch.empty((B, H, Nq, D), dtype=torch.bfloat16, device=q8.device)
-    if lse is None:
-        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q8.device)
+    o, lse = _attn_outputs(o, lse, B, H, Nq, D, q8.device)
     st = _lib.lib().attn_fwd_fp8_rows(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(q_e8m0), _ptr(k_e8m0),
                                       _ptr(v_descale), _ptr(o), _ptr(lse), B, H, Nq, Nkv, D,
                                       float(scale), ctypes_ptr(_stream(q8)))
@@ -425,24 +460,18 @@ def attn_fwd_fp8_rows(q8, k8, v8, q_e8m0, k_e8m0, v_descale, scale=None, o=None,
 def attn_fwd_fp8_rows_v(q8, k8, v8, q_e8m0, k_e8m0, v_e8m0, scale=None, o=None, lse=None):
     """fp8 attention with per-token power-of-two scales for Q, K and V (E8M0
     bytes [B,H,N]) and per-block power-of-two P scales."""
-    _need(q8, "q8", torch.uint8, 4)
-    _need(k8, "k8", torch.uint8, 4)
-    _need(v8, "v8", torch.uint8, 4)
-    _need(q_e8m0, "q_e8m0", torch.uint8)
-    _need(k_e8m0, "k_e8m0", torch.uint8)
-    _need(v_e8m0, "v_e8m0", torch.uint8)
-    B, H, Nq, D = q8.shape
-    Nkv = k8.shape[2]
-    if tuple(k8.shape) != (B, H, Nkv, D) or tuple(v8.shape) != (B, H, Nkv, D):
-        raise ValueError("shape mismatch")
-    if q_e8m0.numel() != B * H * Nq or k_e8m0.numel() != B * H * Nkv or v_e8m0.numel() != B * H * Nkv:
-        raise ValueError("q_e8m0 / k_e8m0 / v_e8m0 must hold one byte per token of each head")
+    B, H, Nq, Nkv, D = _fp8_qkv(q8, k8, v8)
+    for t, name, n in ((q_e8m0, "q_e8m0", B * H * Nq), (k_e8m0, "k_e8m0", B * H * Nkv),
+                       (v_e8m0, "v_e8m0", B * H * Nkv)):
+        if t is None:
+            raise ValueError("%s is required" % name)
+        _out(t, name, torch.uint8, n)
+    _out(o, "o", torch.bfloat16, (B, H, Nq, D))
+    _out(lse, "lse", torch.float32, (B, H, Nq))
+    _gpu(q8=q8, k8=k8, v8=v8, q_e8m0=q_e8m0, k_e8m0=k_e8m0, v_e8m0=v_e8m0, o=o, lse=lse)
     if scale is None:
         scale = D ** -0.5
-    if o is None:
-        o = torch.empty((B, H, Nq, D), dtype=torch.bfloat16, device=q8.device)
-    if lse is None:
-        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q8.device)
+    o, lse = _attn_outputs(o, lse, B, H, Nq, D, q8.device)
     st = _lib.lib().attn_fwd_fp8_rows_v(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(q_e8m0), _ptr(k_e8m0),
                                         _ptr(v_e8m0), _ptr(o), _ptr(lse), B, H, Nq, Nkv, D,
                                         float(scale), ctypes_ptr(_stream(q8)))

@@ -309,6 +309,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_bf16_kernel(
           val = *reinterpret_cast<const u32x4*>(o + q_base + (int64_t)(row0 + r) * D + ch * 8);
         *reinterpret_cast<u32x4*>(stg + r * kPitch + ch * 16) = val;
       }
+      wave_lds_sync();
       // Two-part log-sum-exp merge in the log2 domain, as below.
       const float lc = m_run + log2f(lt);
       const float lr = row < Nq ? lse[li] * kLog2e : -INFINITY;
@@ -338,6 +339,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_bf16_kernel(
         }
       if (g == 0 && row < Nq) lse[li] = (mm + log2f(den)) * kLn2;
     }
+    wave_lds_sync();
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
       const int r = 4 * kk + sub;

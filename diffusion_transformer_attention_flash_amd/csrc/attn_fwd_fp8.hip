@@ -462,6 +462,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_fp8_kernel(
     if (g == 0 && lse != nullptr && row < Nq)
       lse[(int64_t)bh * Nq + row] =
           (m_run + log2f(lt) - (MODE == 2 ? 0.0f : kLog2PScale)) * kLn2;
+    wave_lds_sync();
     // Store kk covers rows 4kk .. 4kk+3 of the wave; lane = 16 * (row % 4) + chunk.
     const int row0 = row - r_lo, sub = 2 * g + (r_lo >> 4), ch = r_lo & 15;
 #pragma unroll

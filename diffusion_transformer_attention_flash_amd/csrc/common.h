@@ -48,6 +48,16 @@ __device__ __forceinline__ float wave_max(float x) {
   return x;
 }
 
+// Orders a wave's LDS writes before its later LDS reads of cells that other
+// lanes of the same wave wrote (wavefront scope: no s_barrier; LDS
+// instructions of one wave complete in order, so this only stops the
+// compiler from moving the accesses across it).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Remap a linear workgroup id so that the workgroups the hardware places on
 // one XCD (ids congruent mod 8) get consecutive logical ids: neighbouring
 // query tiles of one head then run on the same XCD and share its L2.

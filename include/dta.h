@@ -252,7 +252,9 @@ int attn_fwd_fp8(const void* q8, const void* k8, const void* v8,
  * seq_split   the inverse: x = [B,H,sum lens,D] -> parts; tokens lens[p] ..
  *             padded[p]-1 of each part are written as zeros.
  * head_concat parts: part p = [B,heads[p],N,D]; out = [B,sum heads,N,D].
- * head_split  the inverse. heads[p] >= 1.
+ * head_split  the inverse. heads[p] >= 1 for every part: a part with no
+ *             heads is rejected (DTA_EINVAL), as is lens[p] = 0 with padded
+ *             NULL (a part must occupy at least one row).
  * All are 16-byte aligned device buffers. Return DTA_OK, DTA_EINVAL (bad
  * sizes, P out of range, D not a multiple of 8), DTA_EALIGN or DTA_ELAUNCH.
  */

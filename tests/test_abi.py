@@ -149,6 +149,10 @@ def test_layout_validation():
     assert lib.seq_split(GOOD, GOOD, 2, two, None, 1, 2, 100, None) == _lib.DTA_EINVAL  # D % 8
     assert lib.seq_split(GOOD, ODD, 2, two, None, 1, 2, 128, None) == _lib.DTA_EALIGN
     assert lib.head_concat(GOOD, GOOD, 2, zeros, 1, 8, 128, None) == _lib.DTA_EINVAL  # heads >= 1
+    one_empty = (I * 2)(3, 0)                     # a single part with no heads
+    assert lib.head_concat(GOOD, GOOD, 2, one_empty, 1, 8, 128, None) == _lib.DTA_EINVAL
+    assert lib.head_split(GOOD, GOOD, 2, one_empty, 1, 8, 128, None) == _lib.DTA_EINVAL
+    assert lib.seq_concat(GOOD, GOOD, 2, (I * 2)(3, 0), None, 1, 2, 128, None) == _lib.DTA_EINVAL
     assert lib.head_split(None, GOOD, 2, two, 1, 8, 128, None) == _lib.DTA_EINVAL
     assert lib.head_split(ODD, GOOD, 2, two, 1, 8, 128, None) == _lib.DTA_EALIGN
 
@@ -215,3 +219,62 @@ def test_host_tensors_are_rejected():
         dta.residual_diff(q, q)
     with pytest.raises(ValueError, match="GPU"):
         dta.fp8_quant_per_tensor(q)
+
+
+def test_binding_checks_every_output_before_the_device():
+    """A caller-supplied output of the wrong shape or dtype raises, naming
+    it, before any device check or library call (so this runs on host
+    tensors: shapes and dtypes are checked first)."""
+    import torch
+    import diffusion_transformer_attention_flash_amd as dta
+    bf, f32, u8, i32 = torch.bfloat16, torch.float32, torch.uint8, torch.int32
+    q = torch.zeros(1, 2, 8, 64, dtype=bf)
+    q8 = torch.zeros(1, 2, 8, 64, dtype=u8)
+    e8 = torch.zeros(1, 2, 8, dtype=u8)
+    ds3 = torch.zeros(3, dtype=f32)
+    ds1 = torch.zeros(1, dtype=f32)
+    good_o, good_l = torch.zeros(1, 2, 8, 64, dtype=bf), torch.zeros(1, 2, 8, dtype=f32)
+    short_o, short_l = torch.zeros(1, 2, 7, 64, dtype=bf), torch.zeros(1, 2, 7, dtype=f32)
+    cases = [
+        (lambda: dta.attn_fwd(q, q, q, o=short_o), ValueError, "o"),
+        (lambda: dta.attn_fwd(q, q, q, o=good_o.float()), TypeError, "o"),
+        (lambda: dta.attn_fwd(q, q, q, lse=short_l), ValueError, "lse"),
+        (lambda: dta.attn_merge(q[None].expand(2, -1, -1, -1, -1).contiguous(),
+                                good_l[None].expand(2, -1, -1, -1).contiguous(), o=short_o),
+         ValueError, "o"),
+        (lambda: dta.attn_merge(q[None].contiguous(), good_l[None].contiguous(), lse=short_l),
+         ValueError, "lse"),
+        (lambda: dta.attn_fwd_accum(q, q, q, short_o, good_l), ValueError, "o"),
+        (lambda: dta.attn_fwd_accum(q, q, q, good_o, good_l.double()), TypeError, "lse"),
+        (lambda: dta.attn_merge_into(good_o, short_l, good_o, good_l), ValueError, "lse"),
+        (lambda: dta.attn_merge_into(good_o, good_l, short_o, good_l), ValueError, "o_part"),
+        (lambda: dta.residual_diff(q, q, out=torch.zeros(2, dtype=f32)), ValueError, "out"),
+        (lambda: dta.residual_diff(q, q, out=torch.zeros((), dtype=bf)), TypeError, "out"),
+        (lambda: dta.fbcache_step(q, q, 0.1, q.clone(), q, diff=torch.zeros(2, dtype=f32)),
+         ValueError, "diff"),
+        (lambda: dta.fbcache_step(q, q, 0.1, q.clone(), q, use_cache=torch.zeros((), dtype=f32)),
+         TypeError, "use_cache"),
+        (lambda: dta.fp8_quant_per_tensor(q, x8=torch.zeros(10, dtype=u8)), ValueError, "x8"),
+        (lambda: dta.fp8_quant_per_tensor(q, descale=torch.zeros(2, dtype=f32)), ValueError,
+         "descale"),
+        (lambda: dta.fp8_quant_per_tensor_multi([q, q], descale=torch.zeros(1, dtype=f32)),
+         ValueError, "descale"),
+        (lambda: dta.fp8_quant_per_tensor_multi([q], x8s=[torch.zeros(5, dtype=u8)]),
+         ValueError, "x8s[0]"),
+        (lambda: dta.attn_fwd_fp8(q8, q8, q8, ds1), ValueError, "descale"),
+        (lambda: dta.attn_fwd_fp8(q8, q8, q8, ds3, o=short_o), ValueError, "o"),
+        (lambda: dta.attn_fwd_fp8(q8, q8, q8, ds3, lse=good_l.to(bf)), TypeError, "lse"),
+        (lambda: dta.fp8_quant_rows_pow2(q, e8m0=torch.zeros(3, dtype=u8)), ValueError, "e8m0"),
+        (lambda: dta.fp8_quant_rows_pow2(q, x8=torch.zeros(3, dtype=u8)), ValueError, "x8"),
+        (lambda: dta.attn_fwd_fp8_rows(q8, q8, q8, e8, e8, ds3), ValueError, "v_descale"),
+        (lambda: dta.attn_fwd_fp8_rows(q8, q8, q8, e8[:, :1], e8, ds1), ValueError, "q_e8m0"),
+        (lambda: dta.attn_fwd_fp8_rows(q8, q8, q8, e8, e8, ds1, o=short_o), ValueError, "o"),
+        (lambda: dta.attn_fwd_fp8_rows_v(q8, q8, q8, e8, e8, e8[:, :1]), ValueError, "v_e8m0"),
+        (lambda: dta.attn_fwd_fp8_rows_v(q8, q8, q8, e8, e8, e8, lse=short_l), ValueError, "lse"),
+        (lambda: dta.seq_concat(q.view(-1), [4, 4], 1, 2, 64, out=torch.zeros(3, dtype=bf)),
+         ValueError, "out"),
+        (lambda: dta.head_split(q, [1, 1], parts=torch.zeros(3, dtype=bf)), ValueError, "parts"),
+    ]
+    for fn, exc, name in cases:
+        with pytest.raises(exc, match=re.escape(name)):
+            fn()
