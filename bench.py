@@ -1,23 +1,32 @@
 """Benchmark of the diffusion-transformer attention hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--video-reps R]
 
-One step is one pass of the whole hot path over the FLUX.1-dev 1024x1024
-attention shape (B=1, H=24, N=4608 = 512 text + 4096 image tokens, D=128):
+Headline. ``value`` is the bf16 attention rate of ``attn_fwd`` at the
+FLUX.1-dev 1024x1024 attention shape (B=1, H=24, N=4608 = 512 text + 4096
+image tokens, D=128): 4*B*H*N*N*D FLOP divided by the median of that
+launch's HIP-event durations over the K timed steps, with every input already
+resident in HBM. ``video`` gives the same figure at the HunyuanVideo 720p x
+129-frame shape (N = 119056 = 256 text + 33*45*80 video tokens), timed over
+``--video-reps`` launches. Fractions are of MI355X's published dense bf16
+MFMA peak (2.5 PFLOP/s); ``peaks`` adds the peak implied by the CU count and
+the engine clock read on the box.
+
+One step is one pass of the whole hot path over the FLUX shape:
   1. attn_fwd, bf16, over the full K/V                       (O, LSE)
-  2. the ring-step emulation: attn_fwd over 8 seeded uneven contiguous K/V
+  2. one ring's local work: attn_fwd over 8 seeded uneven contiguous K/V
      chunks, then attn_merge of the 8 partials
-  3. the fp8 variant: per-tensor quantisation of Q, K and V (one
-     fp8_quant_per_tensor_multi call, two launches), then attn_fwd_fp8
+  3. the fp8 variant: per-tensor E4M3 quantisation of Q, K and V (one
+     fp8_quant_per_tensor_multi call), then attn_fwd_fp8
   4. residual_diff over two bf16 [1, 4608, 3072] first-block residuals.
-``value`` is the algorithmic attention work of the step (3 passes of
-4*B*H*N*N*D FLOP) divided by the step's wall time with every input already
-resident in HBM; the merge, quantisation and residual-diff kernels are
-inside the timed region. ``roofline`` reports the dominant kernel (bf16
-attn_fwd at the FLUX shape) from HIP events around each of its launches.
-The 119056-token HunyuanVideo shape is timed separately (``video``: bf16 and
-per-tensor fp8 attention).
-``cpu_baseline`` times the float64 CPU oracle on a bounded sample.
+``ms_per_step`` is the whole step's time; every leg is timed with HIP events
+on the launching stream inside the same timed steps (``legs``). The fp8
+attention is reported against the fp8 peak only. The HBM-bound kernels are
+also timed cold (a 512 MB read evicts the MALL between repetitions) beside
+a cold read-only scan and a device copy of the same bytes (``cold``).
+``roofline`` is the dominant kernel, bf16 attn_fwd at the FLUX shape, from
+the mean of the same per-launch events. ``cpu_baseline`` times the float64
+CPU oracle on bounded samples of the five configurations.
 
 Prints ONE JSON line.
 """
@@ -27,16 +36,23 @@ import hashlib
 import json
 import math
 import os
+import statistics
+import subprocess
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "attention TFLOP/s & % MFMA peak at 4608-tok FLUX and 119k-tok video shapes"
-PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
-PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
-PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+# MI355X published dense peaks (AMD specifications).
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_FP8_TFLOPS = 5000.0
+PEAK_HBM_GBS = 8000.0
+# MFMA throughput per CU per engine clock on CDNA4 (dense).
+BF16_FLOP_PER_CLK_CU = 4096
+FP8_FLOP_PER_CLK_CU = 8192
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_bf16_flux_1024_traffic.json")
 KERNEL_SOURCES = ["diffusion_transformer_attention_flash_amd/csrc/attn_fwd.hip",
                   "diffusion_transformer_attention_flash_amd/csrc/common.h"]
@@ -67,34 +83,216 @@ def attn_flop(B, H, Nq, Nkv, D):
     return 4.0 * B * H * Nq * Nkv * D
 
 
-def cpu_baseline(q, k, v, scale, budget_s=12.0):
-    """Time the float64 oracle on whole heads of the FLUX shape, as many heads
-    as fit in about ``budget_s`` seconds (at least one)."""
-    import numpy as np
-    import oracle
-    qc, kc, vc = q.cpu(), k.cpu(), v.cpu()
-    B, H, N, D = q.shape
-    done, t0 = 0, time.perf_counter()
-    while done < H:
-        oracle.attention(qc[:, done:done + 1], kc[:, done:done + 1], vc[:, done:done + 1], scale)
-        done += 1
-        if time.perf_counter() - t0 > budget_s:
+def stats_ms(ts):
+    ts = sorted(ts)
+    return {"median_ms": statistics.median(ts), "min_ms": ts[0], "mean_ms": sum(ts) / len(ts),
+            "max_ms": ts[-1], "reps": len(ts)}
+
+
+# ---- engine clock and CU count, read on the box ---------------------------
+
+def _run(cmd, timeout=20):
+    try:
+        r = subprocess.run(cmd, capture_output=True, text=True, timeout=timeout)
+        return r.stdout
+    except (OSError, subprocess.SubprocessError):
+        return ""
+
+
+def rocminfo_gpu():
+    """(compute units, max engine clock in MHz) of the first gfx950 agent."""
+    cus = mhz = None
+    in_gpu = False
+    for line in _run(["rocminfo"]).splitlines():
+        s = line.strip()
+        if s.startswith("Name:") and "gfx950" in s:
+            in_gpu = True
+        elif s.startswith("Agent ") and in_gpu and cus is not None:
             break
-    dt = time.perf_counter() - t0
-    cores = len(os.sched_getaffinity(0))
-    threads = None
+        if in_gpu and s.startswith("Compute Unit:") and cus is None:
+            cus = int(s.split(":")[1])
+        if in_gpu and s.startswith("Max Clock Freq. (MHz):") and mhz is None:
+            mhz = int(s.split(":")[1])
+    return cus, mhz
+
+
+def current_sclk_mhz():
+    """The engine clock the driver reports right now, in MHz, or None."""
+    import glob
+    import re
+    for f in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            txt = open(f).read()
+        except OSError:
+            continue
+        for line in txt.splitlines():
+            if line.strip().endswith("*"):
+                m = re.search(r"(\d+)\s*[Mm]hz", line)
+                if m:
+                    return int(m.group(1))
+    return None
+
+
+class ClockSampler:
+    """Samples the reported engine clock from a host thread while the GPU
+    runs a long stream of launches; the median is the clock under load."""
+
+    def __init__(self, period_s=0.02):
+        self.period = period_s
+        self.samples = []
+        self._stop = threading.Event()
+        self._t = threading.Thread(target=self._loop, daemon=True)
+
+    def _loop(self):
+        while not self._stop.is_set():
+            v = current_sclk_mhz()
+            if v is not None:
+                self.samples.append(v)
+            time.sleep(self.period)
+
+    def __enter__(self):
+        self._t.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        self._t.join()
+
+    def median(self):
+        return statistics.median(self.samples) if self.samples else None
+
+
+# ---- the CPU oracle baseline ----------------------------------------------
+
+def cpu_info():
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas = threads = None
     try:
         from threadpoolctl import threadpool_info
-        threads = max((p.get("num_threads") or 0) for p in threadpool_info()) or None
+        for p in threadpool_info():
+            if p.get("user_api") == "blas":
+                blas = "%s %s" % (p.get("internal_api"), p.get("version"))
+                threads = p.get("num_threads")
+                break
     except Exception:
         pass
+    return {"cpu_model": model, "cores_available": len(os.sched_getaffinity(0)),
+            "blas": blas, "blas_threads": threads}
+
+
+def cpu_baseline(dev, scale):
+    """The float64 oracle on bounded samples of the five configurations, on
+    the host cores of this machine (BLAS-threaded). About 20-30 s in all."""
+    import numpy as np
+    import torch
+    import oracle
+    import workloads
+    out = {}
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        r = fn()
+        return r, time.perf_counter() - t0
+
+    # C1: the tiny case, all rows, plus its 4-chunk merge.
+    c = workloads.CONFIGS["tiny"]
+    q, k, v = workloads.workload_qkv("tiny")
+    sc = c["D"] ** -0.5
+
+    def c1():
+        oracle.attention(q, k, v, sc)
+        parts = [oracle.attention(q, kc, vc, sc) for kc, vc in workloads.split_kv(k, v, c["chunks"])]
+        oracle.merge(np.stack([p[0] for p in parts]), np.stack([p[1] for p in parts]))
+    _, dt = timed(c1)
+    out["c1_tiny"] = {"s": dt, "sample": "all 2x256 rows, plus the 4x64-key chunked merge"}
+
+    # C2: FLUX bf16, whole heads, as many as fit in ~8 s.
+    c = workloads.CONFIGS["flux_1024"]
+    q, k, v = workloads.workload_qkv("flux_1024")
+    B, H, N, D = c["B"], c["H"], c["N"], c["D"]
+    done, t0 = 0, time.perf_counter()
+    while done < H:
+        oracle.attention(q[:, done:done + 1], k[:, done:done + 1], v[:, done:done + 1], scale)
+        done += 1
+        if time.perf_counter() - t0 > 8.0:
+            break
+    dt = time.perf_counter() - t0
+    c2_tflops = attn_flop(B, done, N, N, D) / dt / 1e12
+    out["c2_flux_1024"] = {"s": dt, "heads": done, "TFLOP/s": c2_tflops,
+                           "sample": "%d of %d heads, all %d rows each" % (done, H, N)}
+
+    # C3: the 8 uneven chunks and their merge, one head.
+    c3 = workloads.CONFIGS["flux_1024_chunked"]
+    lens = workloads.chunk_lengths(c3["config"], N, c3["n_chunks"], c3["min_chunk"])
+
+    def c3f():
+        parts = [oracle.attention(q[:, :1], kc, vc, scale)
+                 for kc, vc in workloads.split_kv(k[:, :1], v[:, :1], lens)]
+        oracle.merge(np.stack([p[0] for p in parts]), np.stack([p[1] for p in parts]))
+    _, dt = timed(c3f)
+    out["c3_flux_8_chunks"] = {"s": dt, "TFLOP/s": attn_flop(B, 1, N, N, D) / dt / 1e12,
+                               "sample": "1 of %d heads: 8 chunk attentions %s + merge" % (H, lens)}
+
+    # C4: the video shape, 256 rows per head (generated on the GPU as the
+    # tests do, copied back head by head), for as many heads as fit in ~8 s.
+    cv = workloads.CONFIGS["hunyuan_720p_129f"]
+    qv, kv, vv = workloads.workload_qkv("hunyuan_720p_129f", device=dev)
+    rows = workloads.sample_rows_per_head(cv["config"], cv["N"], cv["H"], cv["sample_rows"],
+                                          cv["n_text"])
+    done, busy, t0 = 0, 0.0, time.perf_counter()
+    while done < cv["H"]:
+        h = done
+        rt = torch.from_numpy(rows[h]).to(dev)
+        qh, kh, vh = qv[:, h:h + 1, rt].cpu(), kv[:, h:h + 1].cpu(), vv[:, h:h + 1].cpu()
+        t1 = time.perf_counter()
+        oracle.attention(qh, kh, vh, scale)
+        busy += time.perf_counter() - t1
+        done += 1
+        if time.perf_counter() - t0 > 8.0:
+            break
+    del qv, kv, vv
+    nv = cv["N"]
+    flop_rows = attn_flop(1, done, rows.shape[1], nv, cv["D"])
+    out["c4_video"] = {"s": busy, "heads": done, "TFLOP/s": flop_rows / busy / 1e12,
+                       "sample": "%d rows per head x %d of %d heads against all %d keys "
+                                 "(oracle time only, not the host copies)"
+                                 % (rows.shape[1], done, cv["H"], nv),
+                       "extrapolated_full_tensor_s": busy * (nv / rows.shape[1]) * (cv["H"] / done),
+                       "extrapolation": "x(119056/256 rows) x(24/heads): labelled estimate"}
+
+    # C5: the fp8 oracle on one head of the FLUX tensors, and the fp64
+    # residual sum over the whole [1, 4608, 3072] pair.
+    c5 = workloads.CONFIGS["flux_1024_fp8"]
+
+    def c5f():
+        qq, kk, vv8 = (oracle.quant_per_tensor(t[:, :1]) for t in (q, k, v))
+        oracle.attention_fp8(qq[0], kk[0], vv8[0], (qq[1], kk[1], vv8[1]), scale)
+    _, dt = timed(c5f)
+    ra, rb = workloads.residual_pair(c5["config"], c5["residual_shape"], c5["residual_noise"])
+    (_, dt_r) = timed(lambda: oracle.residual_diff(ra, rb))
+    res_bytes = 2 * ra.numel() * 2
+    out["c5_fp8_and_residual"] = {
+        "fp8_s": dt, "fp8_TFLOP/s": attn_flop(B, 1, N, N, D) / dt / 1e12,
+        "residual_s": dt_r, "residual_GB/s": res_bytes / dt_r / 1e9,
+        "sample": "fp8 oracle (quantise + attention) on 1 of %d heads; residual_diff in fp64 "
+                  "over all %d elements" % (H, ra.numel())}
+    info = cpu_info()
     return {
-        "value": attn_flop(B, done, N, N, D) / dt / 1e12,
+        "value": c2_tflops,
         "unit": "TFLOP/s",
-        "cores": threads or cores,
+        "cores": info["blas_threads"] or info["cores_available"],
         "kind": "oracle",
-        "sample": "float64 numpy oracle.attention on %d of %d heads of the FLUX 4608-token "
-                  "shape (all %d query rows each), %.1f s" % (done, H, N, dt),
+        "sample": "float64 numpy oracle.attention on %s of the FLUX 4608-token shape; "
+                  "the other configurations in 'configs'" % out["c2_flux_1024"]["sample"],
+        "configs": out,
+        **info,
     }
 
 
@@ -103,12 +301,12 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--video-reps", type=int, default=3)
+    ap.add_argument("--video-reps", type=int, default=5)
     ap.add_argument("--no-video", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--legs", default="all",
                     help="comma-separated subset of attn,chunks,merge,quant,fp8,residual "
-                         "(profiling runs only; the reported value needs all)")
+                         "(profiling runs only; the step needs all)")
     args = ap.parse_args()
     legs_on = set(["attn", "chunks", "merge", "quant", "fp8", "residual"]
                   if args.legs == "all" else args.legs.split(","))
@@ -116,6 +314,9 @@ def main():
         print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(the ring/Ulysses exchanges are out of scope); run with --gpus 1.",
               file=sys.stderr)
+        sys.exit(2)
+    if args.steps < 1:
+        print("--steps must be >= 1", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -127,6 +328,7 @@ def main():
         sys.exit(2)
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    Ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
 
     c2 = workloads.CONFIGS["flux_1024"]
     c3 = workloads.CONFIGS["flux_1024_chunked"]
@@ -149,109 +351,105 @@ def main():
     ds = torch.empty(3, dtype=torch.float32, device=dev)
     o8 = torch.empty_like(q)
     l8 = torch.empty_like(lse)
-    ra, rb = workloads.residual_pair(c5["config"], c5["residual_shape"], c5["residual_noise"], device=dev)
+    ra, rb = workloads.residual_pair(c5["config"], c5["residual_shape"], c5["residual_noise"],
+                                     device=dev)
     rd = torch.empty((), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
+    if "fp8" in legs_on and "quant" not in legs_on:
+        dta.fp8_quant_per_tensor_multi([q, k, v], [q8, k8, v8], ds)
 
     flop_full = attn_flop(B, H, N, N, D)
-    step_flop = flop_full * sum(1 for x in ("attn", "chunks", "fp8") if x in legs_on)
-    if "fp8" in legs_on and "quant" not in legs_on:
-        for x, x8_, i in ((q, q8, 0), (k, k8, 1), (v, v8, 2)):
-            dta.fp8_quant_per_tensor(x, x8_, ds[i:i + 1])
+    LEGS = ["attn", "chunks", "merge", "quant", "fp8", "residual"]
 
     def step(ev=None):
-        if ev is not None:
-            ev[0].record()
+        def mark(i):
+            if ev is not None:
+                ev[i].record()
+        mark(0)
         if "attn" in legs_on:
             dta.attn_fwd(q, k, v, scale, o=o, lse=lse)
-        if ev is not None:
-            ev[1].record()
+        mark(1)
         if "chunks" in legs_on:
             for i, (kc, vc) in enumerate(chunks):
                 dta.attn_fwd(q, kc, vc, scale, o=o_parts[i], lse=l_parts[i])
-        if ev is not None:
-            ev[2].record()
+        mark(2)
         if "merge" in legs_on:
             dta.attn_merge(o_parts, l_parts, o=o_m, lse=l_m)
-        if ev is not None:
-            ev[3].record()
+        mark(3)
         if "quant" in legs_on:
             dta.fp8_quant_per_tensor_multi([q, k, v], [q8, k8, v8], ds)
-        if ev is not None:
-            ev[4].record()
+        mark(4)
         if "fp8" in legs_on:
             dta.attn_fwd_fp8(q8, k8, v8, ds, scale, o=o8, lse=l8)
-        if ev is not None:
-            ev[5].record()
+        mark(5)
         if "residual" in legs_on:
             dta.residual_diff(ra, rb, out=rd)
-        if ev is not None:
-            ev[6].record()
+        mark(6)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    # Timed region: K whole steps, bracketed by synchronisation.
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
+    # Timed region: K whole steps bracketed by synchronisation. The per-leg
+    # events are recorded on the launching stream inside the same steps.
+    evs = [[Ev() for _ in range(7)] for _ in range(args.steps)]
+    t_start, t_end = Ev(), Ev()
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_start.record()
-    for _ in range(args.steps):
-        step()
+    for i in range(args.steps):
+        step(evs[i])
     t_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_per_step = t_start.elapsed_time(t_end) / args.steps
+    per_leg = {name: [e[j].elapsed_time(e[j + 1]) for e in evs] for j, name in enumerate(LEGS)}
 
-    # Per-leg HIP event timing over a second pass of K steps (same stream).
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-
-    def leg(a, b):
-        return max(sum(e[a].elapsed_time(e[b]) for e in evs) / len(evs), 1e-6)
-
-    ms_attn = leg(0, 1)
-    ms_chunks = leg(1, 2)
-    ms_merge = leg(2, 3)
-    ms_quant = leg(3, 4)
-    ms_fp8 = leg(4, 5)
-    ms_res = leg(5, 6)
+    attn_st = stats_ms(per_leg["attn"])
+    flux_tflops = flop_full / (attn_st["median_ms"] * 1e-3) / 1e12
+    achieved = flop_full / (attn_st["mean_ms"] * 1e-3) / 1e12
     merge_bytes = n_parts * (B * H * N * D * 2 + B * H * N * 4) + B * H * N * D * 2 + B * H * N * 4
     res_bytes = 2 * ra.numel() * 2
     quant_bytes = 3 * (2 * q.numel() * 2 + q.numel())     # amax read + cast read + fp8 write
-    achieved = flop_full / (ms_attn * 1e-3) / 1e12
-    traffic = load_traffic()
 
-    legs = {
-        "attn_fwd_bf16": {"ms": ms_attn, "TFLOP/s": achieved,
-                          "frac_bf16_peak": achieved / PEAK_BF16_TFLOPS},
-        "attn_fwd_bf16_8_chunks": {"ms": ms_chunks, "chunk_lens": lens,
-                                   "TFLOP/s": flop_full / (ms_chunks * 1e-3) / 1e12},
-        "attn_merge": {"ms": ms_merge, "GB/s": merge_bytes / (ms_merge * 1e-3) / 1e9,
-                       "frac_hbm_peak": merge_bytes / (ms_merge * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                       "bytes": merge_bytes, "cache": "warm"},
-        "fp8_quant_x3": {"ms": ms_quant, "GB/s": quant_bytes / (ms_quant * 1e-3) / 1e9,
-                         "bytes": quant_bytes, "cache": "warm"},
-        "attn_fwd_fp8": {"ms": ms_fp8, "TFLOP/s": flop_full / (ms_fp8 * 1e-3) / 1e12,
-                         "frac_fp8_peak": flop_full / (ms_fp8 * 1e-3) / 1e12 / PEAK_FP8_TFLOPS},
-        "residual_diff": {"ms": ms_res, "GB/s": res_bytes / (ms_res * 1e-3) / 1e9,
-                          "frac_hbm_peak": res_bytes / (ms_res * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                          "bytes": res_bytes, "cache": "warm"},
-    }
+    def tf(flop, st):
+        return {"TFLOP/s_median": flop / (st["median_ms"] * 1e-3) / 1e12,
+                "TFLOP/s_best": flop / (st["min_ms"] * 1e-3) / 1e12}
 
-    leg_key = {"attn": "attn_fwd_bf16", "chunks": "attn_fwd_bf16_8_chunks",
-               "merge": "attn_merge", "quant": "fp8_quant_x3", "fp8": "attn_fwd_fp8",
-               "residual": "residual_diff"}
-    legs = {leg_key[x]: legs[leg_key[x]] for x in leg_key if x in legs_on}
+    def gbs(nbytes, st):
+        r = nbytes / (st["median_ms"] * 1e-3) / 1e9
+        return {"GB/s_median": r, "frac_hbm_peak": r / PEAK_HBM_GBS, "bytes": nbytes,
+                "cache": "warm (inside the step)"}
+
+    legs = {}
+    if "attn" in legs_on:
+        legs["attn_fwd_bf16"] = {**attn_st, **tf(flop_full, attn_st),
+                                 "frac_bf16_peak": flux_tflops / PEAK_BF16_TFLOPS}
+    if "chunks" in legs_on:
+        st = stats_ms(per_leg["chunks"])
+        legs["attn_fwd_bf16_8_chunks"] = {**st, **tf(flop_full, st), "chunk_lens": lens,
+                                          "frac_bf16_peak": flop_full / (st["median_ms"] * 1e-3)
+                                          / 1e12 / PEAK_BF16_TFLOPS}
+    if "merge" in legs_on:
+        st = stats_ms(per_leg["merge"])
+        legs["attn_merge"] = {**st, **gbs(merge_bytes, st)}
+    if "quant" in legs_on:
+        st = stats_ms(per_leg["quant"])
+        legs["fp8_quant_qkv"] = {**st, **gbs(quant_bytes, st)}
+    if "fp8" in legs_on:
+        st = stats_ms(per_leg["fp8"])
+        t8 = flop_full / (st["median_ms"] * 1e-3) / 1e12
+        legs["attn_fwd_fp8"] = {**st, **tf(flop_full, st), "frac_fp8_peak": t8 / PEAK_FP8_TFLOPS,
+                                "note": "e4m3 MFMA: against the fp8 peak, never the bf16 one"}
+    if "residual" in legs_on:
+        st = stats_ms(per_leg["residual"])
+        legs["residual_diff"] = {**st, **gbs(res_bytes, st)}
 
     # The HBM-bound kernels once more, each alone and cold: a 512 MB read
-    # between repetitions evicts the 256 MB MALL (a read, so that no dirty
-    # lines are left to write back during the timed kernel). A device copy of
-    # the same byte count gives the bandwidth reachable at these sizes.
+    # between repetitions evicts the 256 MB MALL (a read, so no dirty lines
+    # are written back during the timed kernel). Beside them, the ceilings a
+    # kernel of the same size can reach: a read-only scan (torch's sum over
+    # the same bytes) and a device copy.
     flush = torch.ones(128 << 20, dtype=torch.float32, device=dev)
     fsum = torch.empty((1,), dtype=torch.float32, device=dev)
 
@@ -259,7 +457,7 @@ def main():
         ts = []
         for r in range(reps + 2):
             torch.sum(flush, dim=(0,), out=fsum[0])
-            a_ev, b_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a_ev, b_ev = Ev(), Ev()
             a_ev.record()
             fn()
             b_ev.record()
@@ -270,199 +468,126 @@ def main():
         return ts[len(ts) // 2], ts[0]
 
     cold = {}
+    scan_src = torch.cat([ra.view(-1), rb.view(-1)])
+    scan_out = torch.empty((), dtype=torch.float32, device=dev)
+    cp_dst = torch.empty_like(ra)
+    cases = {}
     if "merge" in legs_on:
-        cold["attn_merge"] = (lambda: dta.attn_merge(o_parts, l_parts, o=o_m, lse=l_m), merge_bytes)
+        cases["attn_merge"] = (lambda: dta.attn_merge(o_parts, l_parts, o=o_m, lse=l_m), merge_bytes)
     if "quant" in legs_on:
-        cold["fp8_quant_q"] = (lambda: dta.fp8_quant_per_tensor(q, q8, ds[0:1]), quant_bytes // 3)
+        cases["fp8_quant_q"] = (lambda: dta.fp8_quant_per_tensor(q, q8, ds[0:1]), quant_bytes // 3)
     if "residual" in legs_on:
-        cold["residual_diff"] = (lambda: dta.residual_diff(ra, rb, out=rd), res_bytes)
-    if cold:
-        cp_dst = torch.empty_like(ra)
-        cold["device_copy_same_bytes_as_residual"] = (lambda: cp_dst.copy_(ra), res_bytes)
-        for name, (fn, nbytes) in cold.items():
-            med, mn = cold_us(fn)
-            legs.setdefault("cold", {})[name] = {
-                "us_median": med, "us_min": mn, "bytes": nbytes,
-                "GB/s_median": nbytes / (med * 1e-6) / 1e9,
-                "frac_hbm_peak": nbytes / (med * 1e-6) / 1e9 / PEAK_HBM_GBS}
-        del cp_dst
-    del flush
+        cases["residual_diff"] = (lambda: dta.residual_diff(ra, rb, out=rd), res_bytes)
+        cases["ceiling_read_only_scan_same_bytes"] = (
+            lambda: torch.sum(scan_src, dim=(0,), dtype=torch.float32, out=scan_out), res_bytes)
+        cases["ceiling_device_copy_same_bytes"] = (lambda: cp_dst.copy_(ra), res_bytes)
+    for name, (fn, nbytes) in cases.items():
+        med, mn = cold_us(fn)
+        cold[name] = {"us_median": med, "us_min": mn, "bytes": nbytes,
+                      "GB/s_median": nbytes / (med * 1e-6) / 1e9,
+                      "frac_hbm_peak": nbytes / (med * 1e-6) / 1e9 / PEAK_HBM_GBS}
+    if "residual_diff" in cold:
+        cold["residual_diff"]["vs_read_only_scan"] = (
+            cold["ceiling_read_only_scan_same_bytes"]["us_median"] / cold["residual_diff"]["us_median"])
+    del flush, scan_src, cp_dst
 
-    # First Block Cache step on the device (residual_diff + decision + the
-    # guarded hidden += cached) at the FLUX residual shape, once with a
-    # threshold that reuses the cache and once with one that does not.
-    if "residual" in legs_on:
-        hid = torch.zeros_like(ra)
-        cac = torch.full_like(ra, 2.0 ** -9)
-        fd = torch.empty((), dtype=torch.float32, device=dev)
-        fu = torch.empty((), dtype=torch.int32, device=dev)
-        fb = {}
-        for label, thr in (("reuse", 1.0), ("recompute", 0.0)):
-            fn = (lambda t: (lambda: dta.fbcache_step(ra, rb, t, hid, cac, diff=fd, use_cache=fu)))(thr)
-            for _ in range(3):
-                fn()
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            for _ in range(args.steps):
-                fn()
-            e1.record()
-            torch.cuda.synchronize()
-            us = e0.elapsed_time(e1) / args.steps * 1e3
-            nbytes = res_bytes + (3 * ra.numel() * 2 if label == "reuse" else 0)
-            fb[label] = {"us": us, "use_cache": int(fu.item()), "bytes": nbytes,
-                         "GB/s": nbytes / (us * 1e-6) / 1e9}
-        fb["in_step"] = False
-        legs["fbcache_step"] = fb
-        del hid, cac
-
-    # Row-wise fp8 at the FLUX shape, outside the step: per-token power-of-two
-    # Q/K scales applied by the MFMA operand scales with per-tensor V
-    # (attn_fwd_fp8_rows), and with per-token V scales folded into per-block
-    # scaled P (attn_fwd_fp8_rows_v).
-    if "fp8" in legs_on:
-        rq8 = torch.empty_like(q8)
-        rk8 = torch.empty_like(q8)
-        rv8 = torch.empty_like(q8)
-        req = torch.empty((B, H, N), dtype=torch.uint8, device=dev)
-        rek = torch.empty_like(req)
-        rev = torch.empty_like(req)
-        ro = torch.empty_like(q)
-        rl = torch.empty_like(lse)
-        dta.fp8_quant_rows_pow2(v, x8=rv8, e8m0=rev)
-        rows_legs = {}
-        for name, fn in (
-                ("quant_rows_q_and_k", lambda: (dta.fp8_quant_rows_pow2(q, x8=rq8, e8m0=req),
-                                                dta.fp8_quant_rows_pow2(k, x8=rk8, e8m0=rek))),
-                ("attn_fwd_fp8_rows_v", lambda: dta.attn_fwd_fp8_rows_v(rq8, rk8, rv8, req, rek, rev,
-                                                                        scale, o=ro, lse=rl)),
-                ("attn_fwd_fp8_rows", lambda: dta.attn_fwd_fp8_rows(rq8, rk8, v8, req, rek, ds[2:3],
-                                                                    scale, o=ro, lse=rl))):
-            for _ in range(3):
-                fn()
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            for _ in range(args.steps):
-                fn()
-            e1.record()
-            torch.cuda.synchronize()
-            ms = e0.elapsed_time(e1) / args.steps
-            rows_legs[name] = {"ms": ms}
-        qb = 2 * (q.numel() * 2 + q.numel() + B * H * N)
-        rows_legs["quant_rows_q_and_k"]["GB/s"] = qb / (rows_legs["quant_rows_q_and_k"]["ms"] * 1e-3) / 1e9
-        for kname in ("attn_fwd_fp8_rows", "attn_fwd_fp8_rows_v"):
-            tf = flop_full / (rows_legs[kname]["ms"] * 1e-3) / 1e12
-            rows_legs[kname]["TFLOP/s"] = tf
-            rows_legs[kname]["frac_fp8_peak"] = tf / PEAK_FP8_TFLOPS
-        rows_legs["in_step"] = False
-        legs["fp8_rows"] = rows_legs
-        del rq8, rk8, rv8, req, rek, rev, ro, rl
-
-    # Layout kernels of context parallelism at the FLUX tensor size (P = 8):
-    # Ulysses' head split of Q for the all-to-all, and the token concat of 8
-    # received parts. Each moves 28.3 MB in and 28.3 MB out.
-    if "attn" in legs_on:
-        lay = {}
-        heads8 = [H // 8] * 8
-        toks8 = [N // 8] * 8
-        buf_h = torch.empty(q.numel(), dtype=torch.bfloat16, device=dev)
-        out_s = torch.empty_like(q)
-        for name, fn in (("head_split_P8", lambda: dta.head_split(q, heads8, parts=buf_h)),
-                         ("seq_concat_P8", lambda: dta.seq_concat(buf_h, toks8, B, H, D, out=out_s))):
-            for _ in range(3):
-                fn()
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            for _ in range(args.steps):
-                fn()
-            e1.record()
-            torch.cuda.synchronize()
-            us = e0.elapsed_time(e1) / args.steps * 1e3
-            nbytes = 2 * q.numel() * 2
-            lay[name] = {"us": us, "bytes": nbytes, "GB/s": nbytes / (us * 1e-6) / 1e9,
-                         "frac_hbm_peak": nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS}
-        lay["in_step"] = False
-        legs["layout"] = lay
-        del buf_h, out_s
-
-    # The same ring with the merge fused into each step (attn_fwd_accum): the
-    # first chunk by attn_fwd, the other seven folded into one running (o, lse).
-    # Timed apart from the step, which keeps the separate partials + merge.
+    # The fused 8-step ring (attn_fwd_accum), apart from the step.
+    ring = None
     if "chunks" in legs_on:
         o_r = torch.empty_like(q)
         l_r = torch.empty_like(lse)
 
-        def ring():
+        def ring_fn():
             dta.attn_fwd(q, chunks[0][0], chunks[0][1], scale, o=o_r, lse=l_r)
             for kc, vc in chunks[1:]:
                 dta.attn_fwd_accum(q, kc, vc, o_r, l_r, scale)
 
         for _ in range(3):
-            ring()
-        torch.cuda.synchronize()
-        ra_ev, rb_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        ra_ev.record()
+            ring_fn()
+        ts = []
         for _ in range(args.steps):
-            ring()
-        rb_ev.record()
+            a_ev, b_ev = Ev(), Ev()
+            a_ev.record()
+            ring_fn()
+            b_ev.record()
+            ts.append((a_ev, b_ev))
         torch.cuda.synchronize()
-        ms_ring = ra_ev.elapsed_time(rb_ev) / args.steps
-        legs["ring_fused_8_steps"] = {
-            "ms": ms_ring, "TFLOP/s": flop_full / (ms_ring * 1e-3) / 1e12,
-            "vs_chunks_plus_merge_ms": ms_chunks + ms_merge,
-            "in_step": False}
+        st = stats_ms([a.elapsed_time(b) for a, b in ts])
+        ring = {**st, **tf(flop_full, st)}
         del o_r, l_r
+    del chunks
+
+    # The HunyuanVideo shape: bf16 and per-tensor fp8, >= 5 launches each;
+    # the engine clock is sampled while the bf16 launches run.
+    cus, max_mhz = rocminfo_gpu()
     video = None
+    load_mhz = None
     if not args.no_video:
-        del chunks
         cv = workloads.CONFIGS["hunyuan_720p_129f"]
         qv, kv, vv = workloads.workload_qkv("hunyuan_720p_129f", device=dev)
         ov = torch.empty_like(qv)
         lv = torch.empty((cv["B"], cv["H"], cv["N"]), dtype=torch.float32, device=dev)
-        dta.attn_fwd(qv, kv, vv, cv["D"] ** -0.5, o=ov, lse=lv)
-        torch.cuda.synchronize()
-        ts = []
-        for _ in range(max(1, args.video_reps)):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            dta.attn_fwd(qv, kv, vv, cv["D"] ** -0.5, o=ov, lse=lv)
-            b.record()
-            torch.cuda.synchronize()
-            ts.append(a.elapsed_time(b))
-        ms_v = sorted(ts)[len(ts) // 2]
+        sv = cv["D"] ** -0.5
         fv = attn_flop(cv["B"], cv["H"], cv["N"], cv["N"], cv["D"])
-        video = {"workload": "hunyuan_720p_129f (B=1, H=24, N=119056, D=128, bf16)",
-                 "ms": ms_v, "TFLOP/s": fv / (ms_v * 1e-3) / 1e12,
-                 "frac_bf16_peak": fv / (ms_v * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-                 "reps": len(ts)}
-        # The per-tensor fp8 attention at the same shape (quantisation outside
-        # the timed launches).
+        dta.attn_fwd(qv, kv, vv, sv, o=ov, lse=lv)
+        torch.cuda.synchronize()
+        reps = max(5, args.video_reps)
+        with ClockSampler() as clk:
+            pairs = []
+            for _ in range(reps):
+                a_ev, b_ev = Ev(), Ev()
+                a_ev.record()
+                dta.attn_fwd(qv, kv, vv, sv, o=ov, lse=lv)
+                b_ev.record()
+                pairs.append((a_ev, b_ev))
+            torch.cuda.synchronize()
+        load_mhz = clk.median()
+        st = stats_ms([a.elapsed_time(b) for a, b in pairs])
+        video = {"workload": "hunyuan_720p_129f: B=1, H=24, N=119056 (256 text + 33x45x80 "
+                             "video tokens), D=128, bf16 attn_fwd",
+                 **st, **tf(fv, st),
+                 "frac_bf16_peak": fv / (st["median_ms"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
         (q8v, k8v, v8v), dsv = dta.fp8_quant_per_tensor_multi([qv, kv, vv])
         del qv, kv, vv
-        dta.attn_fwd_fp8(q8v, k8v, v8v, dsv, cv["D"] ** -0.5, o=ov, lse=lv)
+        dta.attn_fwd_fp8(q8v, k8v, v8v, dsv, sv, o=ov, lse=lv)
         torch.cuda.synchronize()
-        ts = []
-        for _ in range(max(1, args.video_reps)):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            dta.attn_fwd_fp8(q8v, k8v, v8v, dsv, cv["D"] ** -0.5, o=ov, lse=lv)
-            b.record()
-            torch.cuda.synchronize()
-            ts.append(a.elapsed_time(b))
-        ms_v8 = sorted(ts)[len(ts) // 2]
-        video["fp8_per_tensor"] = {"ms": ms_v8, "TFLOP/s": fv / (ms_v8 * 1e-3) / 1e12,
-                                   "frac_fp8_peak": fv / (ms_v8 * 1e-3) / 1e12 / PEAK_FP8_TFLOPS}
+        pairs = []
+        for _ in range(reps):
+            a_ev, b_ev = Ev(), Ev()
+            a_ev.record()
+            dta.attn_fwd_fp8(q8v, k8v, v8v, dsv, sv, o=ov, lse=lv)
+            b_ev.record()
+            pairs.append((a_ev, b_ev))
+        torch.cuda.synchronize()
+        st = stats_ms([a.elapsed_time(b) for a, b in pairs])
+        video["fp8_per_tensor"] = {**st, **tf(fv, st),
+                                   "frac_fp8_peak": fv / (st["median_ms"] * 1e-3) / 1e12
+                                   / PEAK_FP8_TFLOPS}
         del q8v, k8v, v8v, ov, lv
+
+    n_cu = cus or torch.cuda.get_device_properties(dev).multi_processor_count
+    peaks = {"published_bf16_TFLOP/s": PEAK_BF16_TFLOPS, "published_fp8_TFLOP/s": PEAK_FP8_TFLOPS,
+             "compute_units": n_cu, "max_engine_clock_MHz": max_mhz,
+             "engine_clock_under_load_MHz": load_mhz,
+             "clock_source": "rocminfo (max); the driver's current engine-clock level sampled "
+                             "while the video launches ran (under load)"}
+    if max_mhz:
+        peaks["bf16_TFLOP/s_at_max_clock"] = n_cu * max_mhz * 1e6 * BF16_FLOP_PER_CLK_CU / 1e12
+    if load_mhz:
+        p_load = n_cu * load_mhz * 1e6 * BF16_FLOP_PER_CLK_CU / 1e12
+        peaks["bf16_TFLOP/s_at_load_clock"] = p_load
+        peaks["flux_frac_of_load_clock_peak"] = flux_tflops / p_load
+        if video:
+            peaks["video_frac_of_load_clock_peak"] = video["TFLOP/s_median"] / p_load
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(q, k, v, scale)
+        cpu = cpu_baseline(dev, scale)
 
+    traffic = load_traffic()
     out = {
         "metric": METRIC,
-        "value": step_flop / (ms_per_step * 1e-3) / 1e12,
+        "value": flux_tflops,
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -474,15 +599,27 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": "flux_1024: B=1, H=24, N=4608 (512 text + 4096 image tokens), D=128; "
-                        "step = bf16 attention + 8-chunk ring-step emulation with merge + "
-                        "fp8 (e4m3) quantise-and-attend + residual_diff on [1,4608,3072]",
+            "workload": "flux_1024: bf16 attn_fwd, B=1, H=24, N=4608 (512 text + 4096 image "
+                        "tokens), D=128, QK-normalised N(0,1) Q/K, N(0,1) V; value = 4*B*H*N*N*D "
+                        "FLOP / median launch time over the timed steps",
+            "step": "bf16 attention + 8-chunk ring-step (8 attn_fwd + attn_merge) + per-tensor "
+                    "fp8 quantise-and-attend + residual_diff on [1,4608,3072]",
             "global_batch": B,
             "seq_len": N,
             "heads": H,
             "head_dim": D,
-            "step_attention_flop": step_flop,
             "parallelism": "single GPU",
+        },
+        "headline": {
+            "flux_1024_bf16": {"TFLOP/s_median": flux_tflops,
+                               "TFLOP/s_best": flop_full / (attn_st["min_ms"] * 1e-3) / 1e12,
+                               "frac_bf16_peak": flux_tflops / PEAK_BF16_TFLOPS,
+                               "median_ms": attn_st["median_ms"], "min_ms": attn_st["min_ms"],
+                               "reps": attn_st["reps"]},
+            "video_bf16": None if video is None else {
+                "TFLOP/s_median": video["TFLOP/s_median"], "TFLOP/s_best": video["TFLOP/s_best"],
+                "frac_bf16_peak": video["frac_bf16_peak"], "median_ms": video["median_ms"],
+                "min_ms": video["min_ms"], "reps": video["reps"]},
         },
         "roofline": {
             "kernel": "attn_fwd_bf16_kernel (flux_1024)",
@@ -492,9 +629,13 @@ def main():
             "unit": "TFLOP/s",
             "frac": achieved / PEAK_BF16_TFLOPS,
             "traffic": traffic,
+            "basis": "4*B*H*N*N*D FLOP per launch / mean HIP-event launch time over the timed steps",
         },
         "cpu_baseline": cpu,
+        "peaks": peaks,
         "legs": legs,
+        "cold": cold,
+        "ring_fused_8_steps": ring,
         "video": video,
         "wall_s_timed": wall,
     }
