@@ -20,10 +20,19 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-// Workspace of the two grid-wide reductions: one partial (two doubles) per
-// workgroup of their fixed grid.
+// Workspace of the grid-wide reductions: per-workgroup partials of their
+// fixed grids (kRedBlocks partial maxima per tensor for the fp8 amax, or
+// kResBlocks float64 pairs for the residual sums), then, at kCounterOffset,
+// the residual sums' arrival counters: one top counter and kResGroups group
+// counters, each on its own 256-byte line. The counters must be zero before
+// a call and are zero again after it.
 constexpr int kRedBlocks = 1024;
-constexpr size_t kWsBytes = sizeof(double) * 2 * kRedBlocks;
+constexpr int kResBlocks = 512;
+constexpr int kResGroups = 16;
+constexpr size_t kCounterOffset = 16384;
+constexpr size_t kWsBytes = kCounterOffset + 256 * (1 + kResGroups);
+static_assert(sizeof(double) * 2 * kResBlocks <= kCounterOffset, "residual partials fit");
+static_assert(kResBlocks % kResGroups == 0, "equal groups");
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);

@@ -11,17 +11,23 @@
 //   the same two launches.
 //
 // The two grid-wide reductions (residual sums, fp8 amax) are HBM-bound scans.
-// A fixed grid of kRedBlocks workgroups strides over the tensor in 16-byte
-// chunks (two chunks per thread per step, so that four 128-bit loads are in
-// flight), reduces in registers, then across the wave and the workgroup, and
-// writes one partial per workgroup to the workspace. The next kernel combines
-// the partials: for the residual sums a one-workgroup kernel, in a fixed
-// order in float64; for the amax every workgroup of the cast kernel, with an
-// integer max (order-free). The kernel boundary, not a device-scope fence,
-// publishes the partials: on gfx950 such a fence writes back the whole L2 of
-// the XCD, and one per workgroup costs more than the scan itself. The results
-// are independent of scheduling and bitwise reproducible, and the workspace
-// needs no initialisation.
+// A fixed grid strides over the tensor in 16-byte chunks (two chunks per
+// thread per step, so that four 128-bit loads are in flight), reduces in
+// registers, then across the wave and the workgroup.
+// * Residual sums (kResBlocks workgroups): each workgroup publishes its
+//   partial pair with device-scope stores (which complete only where every
+//   XCD sees them, so no L2 writeback is needed), waits for them to
+//   complete, then counts itself in with a device-scope atomic add on its
+//   group's counter (kResGroups counters on separate lines: one counter
+//   for all workgroups serialises their adds and cost 10 us). The last of a
+//   group counts the group in on the top counter; the last of those sums all
+//   partials with device-scope loads in a fixed order in float64, writes the
+//   result and returns every counter it used to zero. One launch, and the
+//   result does not depend on which workgroup finishes last.
+// * fp8 amax: every workgroup of the following cast kernel combines the
+//   partial maxima itself with an integer max (order-free); the kernel
+//   boundary publishes them.
+// Both are bitwise reproducible.
 
 #include <algorithm>
 
@@ -54,9 +60,14 @@ __device__ __forceinline__ void abs_diff_acc(uint32_t a, uint32_t b, float& num,
   den += fabsf(b0) + fabsf(b1);
 }
 
+// Sum|a-b| and sum|b| per workgroup; the last workgroup to arrive finishes:
+// out = float(sum num / sum den) (FBCACHE: also *use_cache = out < threshold,
+// a NaN giving 0).
+template <bool FBCACHE>
 __global__ __launch_bounds__(256) void residual_diff_kernel(
     const uint16_t* __restrict__ a, const uint16_t* __restrict__ b, int64_t n,
-    double* __restrict__ part) {
+    double* __restrict__ part, unsigned* __restrict__ counter, float* __restrict__ out,
+    float threshold, int* __restrict__ use_cache) {
   const int64_t n8 = n >> 3;
   const int64_t stride = (int64_t)gridDim.x * 256;
   const u32x4* a4 = reinterpret_cast<const u32x4*>(a);
@@ -84,46 +95,37 @@ __global__ __launch_bounds__(256) void residual_diff_kernel(
     den += fabsf(bv);
   }
   block_sum2(num, den);
+  __shared__ bool last;
   if (threadIdx.x == 0) {
-    part[2 * blockIdx.x] = (double)num;
-    part[2 * blockIdx.x + 1] = (double)den;
-  }
-}
-
-// One workgroup: fixed-order float64 sum of the kRedBlocks partial pairs --
-// thread t adds partials t, t+256, ..., then a fixed binary tree.
-__global__ __launch_bounds__(256) void residual_diff_finish_kernel(
-    const double* __restrict__ part, float* __restrict__ out) {
-  __shared__ double fx[256], fy[256];
-  double x = 0.0, y = 0.0;
-  for (int p = threadIdx.x; p < kRedBlocks; p += 256) {
-    x += part[2 * p];
-    y += part[2 * p + 1];
-  }
-  fx[threadIdx.x] = x;
-  fy[threadIdx.x] = y;
-  __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if (threadIdx.x < s) {
-      fx[threadIdx.x] += fx[threadIdx.x + s];
-      fy[threadIdx.x] += fy[threadIdx.x + s];
+    __hip_atomic_store(&part[2 * blockIdx.x], (double)num, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&part[2 * blockIdx.x + 1], (double)den, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    // Both stores have completed at device scope before this workgroup is
+    // counted: whoever counts last then reads them.
+    __builtin_amdgcn_s_waitcnt(0);
+    constexpr unsigned kPer = kResBlocks / kResGroups;
+    unsigned* group = counter + 64 * (1 + blockIdx.x % kResGroups);
+    bool l = false;
+    if (__hip_atomic_fetch_add(group, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+        kPer - 1) {
+      // Every workgroup of the group has counted in: reset its counter for
+      // the next call and count the group in.
+      __hip_atomic_store(group, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      l = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+          kResGroups - 1;
     }
-    __syncthreads();
+    last = l;
   }
-  if (threadIdx.x == 0) *out = (float)(fx[0] / fy[0]);
-}
-
-// First Block Cache: the same fixed-order finish, then the decision
-// diff < threshold (float32; a NaN diff or threshold gives 0) into a device
-// flag that the apply kernel reads -- no host round trip.
-__global__ __launch_bounds__(256) void fbcache_finish_kernel(
-    const double* __restrict__ part, float threshold, float* __restrict__ diff,
-    int* __restrict__ use_cache) {
+  __syncthreads();
+  if (!last) return;
+  // Fixed-order float64 sum of the partial pairs: thread t adds partials t,
+  // t+256, ..., then a fixed binary tree.
   __shared__ double fx[256], fy[256];
   double x = 0.0, y = 0.0;
-  for (int p = threadIdx.x; p < kRedBlocks; p += 256) {
-    x += part[2 * p];
-    y += part[2 * p + 1];
+  for (int p = threadIdx.x; p < (int)gridDim.x; p += 256) {
+    x += __hip_atomic_load(&part[2 * p], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    y += __hip_atomic_load(&part[2 * p + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   fx[threadIdx.x] = x;
   fy[threadIdx.x] = y;
@@ -137,8 +139,9 @@ __global__ __launch_bounds__(256) void fbcache_finish_kernel(
   }
   if (threadIdx.x == 0) {
     const float d = (float)(fx[0] / fy[0]);
-    *diff = d;
-    *use_cache = (d < threshold) ? 1 : 0;
+    *out = d;
+    if constexpr (FBCACHE) *use_cache = (d < threshold) ? 1 : 0;
+    __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -178,7 +181,8 @@ __device__ __forceinline__ uint32_t amax_bits(uint32_t w, uint32_t m) {
 // are assigned tensor by tensor: blocks [t * per, (t + 1) * per) serve tensor
 // t, so every tensor keeps the grid a single-tensor call would use.
 constexpr int kQuantMax = 4;
-static_assert(kQuantMax * kRedBlocks * sizeof(uint32_t) <= kWsBytes, "amax partials fit ws");
+static_assert(kQuantMax * kRedBlocks * sizeof(uint32_t) <= kCounterOffset,
+              "amax partials fit ws below the residual counter");
 struct QuantTable {
   const uint16_t* x[kQuantMax];
   uint8_t* x8[kQuantMax];
@@ -335,17 +339,18 @@ static bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) =
 
 extern "C" size_t dta_ws_bytes(void) { return kWsBytes; }
 
+static unsigned* ws_counter(void* ws) {
+  return reinterpret_cast<unsigned*>(static_cast<char*>(ws) + kCounterOffset);
+}
+
 extern "C" int residual_diff(const void* a, const void* b, int64_t n, float* out,
                              void* ws, hipStream_t stream) {
   if (!a || !b || !out || !ws || n < 1) return DTA_EINVAL;
   if (!al16(a) || !al16(b) || !al16(ws) || (reinterpret_cast<uintptr_t>(out) & 3))
     return DTA_EALIGN;
-  double* part = static_cast<double*>(ws);
-  hipLaunchKernelGGL(residual_diff_kernel, dim3(kRedBlocks), dim3(256), 0, stream,
-                     static_cast<const uint16_t*>(a), static_cast<const uint16_t*>(b),
-                     n, part);
-  if (hipGetLastError() != hipSuccess) return DTA_ELAUNCH;
-  hipLaunchKernelGGL(residual_diff_finish_kernel, dim3(1), dim3(256), 0, stream, part, out);
+  hipLaunchKernelGGL(residual_diff_kernel<false>, dim3(kResBlocks), dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(a), static_cast<const uint16_t*>(b), n,
+                     static_cast<double*>(ws), ws_counter(ws), out, 0.0f, nullptr);
   return hipGetLastError() == hipSuccess ? DTA_OK : DTA_ELAUNCH;
 }
 
@@ -357,13 +362,9 @@ extern "C" int fbcache_step(const void* r, const void* r_prev, int64_t n, float 
   if (!al16(r) || !al16(r_prev) || !al16(hidden) || !al16(cached) || !al16(ws) ||
       (reinterpret_cast<uintptr_t>(diff) & 3) || (reinterpret_cast<uintptr_t>(use_cache) & 3))
     return DTA_EALIGN;
-  double* part = static_cast<double*>(ws);
-  hipLaunchKernelGGL(residual_diff_kernel, dim3(kRedBlocks), dim3(256), 0, stream,
-                     static_cast<const uint16_t*>(r), static_cast<const uint16_t*>(r_prev),
-                     n, part);
-  if (hipGetLastError() != hipSuccess) return DTA_ELAUNCH;
-  hipLaunchKernelGGL(fbcache_finish_kernel, dim3(1), dim3(256), 0, stream, part, threshold,
-                     diff, use_cache);
+  hipLaunchKernelGGL(residual_diff_kernel<true>, dim3(kResBlocks), dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(r), static_cast<const uint16_t*>(r_prev), n,
+                     static_cast<double*>(ws), ws_counter(ws), diff, threshold, use_cache);
   if (hipGetLastError() != hipSuccess) return DTA_ELAUNCH;
   const int64_t want = ((n_hidden >> 3) + 255) / 256;
   const unsigned grid = (unsigned)(want < 1 ? 1 : (want < 8192 ? want : 8192));

@@ -16,7 +16,9 @@
  * - bf16 means IEEE-style bfloat16 (1-8-7) stored as uint16; fp8 means OCP
  *   E4M3FN bytes (bias 7, no infinities, max finite 448).
  * - Two calls that share one workspace `ws` must not run concurrently (on
- *   two streams); calls on one stream are ordered and may share it.
+ *   two streams); calls on one stream are ordered and may share it. A
+ *   workspace is dta_ws_bytes() bytes of device memory, zero-filled once
+ *   before its first use; every call leaves it fit for the next one.
  */
 #ifndef DTA_H_
 #define DTA_H_
@@ -138,12 +140,14 @@ int attn_merge_into(void* o, float* lse, const void* o_part,
  * finish, so the result is bitwise reproducible. sum|b| = 0 gives the IEEE
  * quotient (+inf or NaN). The threshold compare is the caller's, or
  * fbcache_step's, which fuses it with the cached-residual apply.
- * Enqueues two kernels (partials, then a one-workgroup finish).
+ * Enqueues one kernel: every workgroup writes its partial sums to ws, and
+ * the last workgroup to finish adds them up and writes out.
  *
  * a, b  bf16 [n], 16-byte aligned; n >= 1
  * out   float, one device scalar, written
- * ws    device workspace of at least dta_ws_bytes() bytes, 16-byte aligned;
- *       scratch for the per-workgroup partials, no initialisation needed.
+ * ws    device workspace of at least dta_ws_bytes() bytes, 16-byte aligned,
+ *       zero-filled once before its first use (it holds the per-workgroup
+ *       partials and an arrival counter that each call returns to zero).
  */
 int residual_diff(const void* a, const void* b, int64_t n, float* out,
                   void* ws, hipStream_t stream);
@@ -160,9 +164,9 @@ int residual_diff(const void* a, const void* b, int64_t n, float* out,
  *     if use:  hidden[i] = bf16(hidden[i] + cached[i])  (float32 sum, rounded
  *                                                      once, to nearest even)
  * `use` is written to *use_cache (0 or 1) for later device-side work; hidden
- * is untouched when it is 0. Enqueues three kernels: residual partials, the
- * finish with the decision, and the apply (whose workgroups leave at once
- * when use = 0).
+ * is untouched when it is 0. Enqueues two kernels: residual_diff's (whose
+ * last workgroup also takes the decision) and the apply (whose workgroups
+ * leave at once when use = 0).
  *
  * r, r_prev   bf16 [n], 16-byte aligned; n >= 1 (this and the previous
  *             step's first-block residual)
@@ -185,7 +189,8 @@ int fbcache_step(const void* r, const void* r_prev, int64_t n, float threshold,
  * x        bf16 [n], 16-byte aligned; n >= 1
  * x8       uint8 [n], 16-byte aligned, written
  * descale  float, one device scalar, written with s
- * ws       as for residual_diff (may be the same buffer, not concurrently)
+ * ws       as for residual_diff (may be the same buffer, not concurrently;
+ *          the quantisers leave residual_diff's counter untouched)
  * Enqueues two kernels: partial maxima into ws, and the cast, every
  * workgroup of which reduces the partials itself; workgroup 0 writes
  * descale.
@@ -330,7 +335,8 @@ int attn_fwd_fp8_rows_v(const void* q8, const void* k8, const void* v8,
                         void* o, float* lse, int B, int H, int Nq, int Nkv, int D,
                         float scale, hipStream_t stream);
 
-/* Bytes of the workspace residual_diff and the per-tensor quantisers need. */
+/* Bytes of the workspace residual_diff, fbcache_step and the per-tensor
+ * quantisers need (zero-filled once before first use). */
 size_t dta_ws_bytes(void);
 
 /* A static, human-readable name of a dta_status value. */

@@ -150,3 +150,30 @@ def test_reductions_on_two_streams():
             assert torch.equal(val[0], x8) and torch.equal(val[1], s)
         else:
             assert torch.equal(val, r1 if what == "r1" else r2), what
+
+
+def test_residual_diff_last_workgroup_finish_repeats():
+    """One launch per call: the workgroup that arrives last sums every
+    partial. Fifty calls in a row (interleaved with per-tensor quantisations
+    that share the workspace) give the same bits and agree with the oracle,
+    and the workspace's arrival counter is back at zero after them."""
+    print("CASE residual_diff repeated, shared workspace", flush=True)
+    import diffusion_transformer_attention_flash_amd._lib as L
+    a, b = workloads.residual_pair(5, (1, 4608, 3072), 0.08, device=DEV)
+    x = torch.randn(3, 1000, 77, device=DEV).to(torch.bfloat16)
+    outs = []
+    for i in range(50):
+        outs.append(dta.residual_diff(a, b).clone())
+        if i % 7 == 3:
+            dta.fp8_quant_per_tensor(x)
+    torch.cuda.synchronize()
+    first = outs[0].item()
+    assert all(o.item() == first for o in outs) and math.isfinite(first)
+    ref = oracle.residual_diff(a.cpu(), b.cpu())
+    assert abs(first - ref) <= RESIDUAL_REL * ref
+    # The workspace holds 16 KB of partials, then the arrival counters (a top
+    # counter and one per group of workgroups, 256 bytes apart): all zero.
+    ws = dta.workspace(DEV)
+    n_ws = int(L.lib().dta_ws_bytes())
+    assert n_ws > 16384
+    assert int(ws[16384:n_ws].count_nonzero().item()) == 0
