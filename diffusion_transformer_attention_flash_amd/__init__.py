@@ -11,6 +11,7 @@ kernels; there is no fallback path -- a missing library raises.
     attn_fwd_accum(q, k, v, o, lse)       one ring step, merged into (o, lse)
     attn_merge_into(o, lse, o_part, lse_part)  pairwise in-place merge
     residual_diff(a, b)                   -> device float32 scalar
+    residual_diff_noalloc(a, b, out)      the same, no workspace (library scratch)
     fbcache_step(r, r_prev, thr, hidden, cached) -> (diff, use_cache) on device
     seq_concat / seq_split / head_concat / head_split   layout permutations
     fp8_quant_per_tensor(x)               -> (x8 uint8, descale float32[1])
@@ -31,6 +32,7 @@ from . import _lib
 from ._lib import DtaError  # noqa: F401
 
 __all__ = ["attn_fwd", "attn_merge", "attn_fwd_accum", "attn_merge_into", "residual_diff",
+           "residual_diff_noalloc",
            "fbcache_step", "seq_concat", "seq_split", "head_concat", "head_split",
            "fp8_quant_rows_pow2", "attn_fwd_fp8_rows", "attn_fwd_fp8_rows_v",
            "fp8_quant_per_tensor", "fp8_quant_per_tensor_multi",
@@ -203,6 +205,25 @@ def residual_diff(a, b, out=None):
     st = _lib.lib().residual_diff(_ptr(a), _ptr(b), a.numel(), _ptr(out), _ptr(ws),
                                   ctypes_ptr(_stream(a)))
     _lib.check("residual_diff", st)
+    return out
+
+
+def residual_diff_noalloc(a, b, out):
+    """residual_diff without a workspace: the library's own scratch array
+    (for callers that cannot allocate; calls on one GPU must not overlap).
+    ``out`` is a caller-allocated float32 device scalar."""
+    _need(a, "a", torch.bfloat16)
+    _need(b, "b", torch.bfloat16)
+    if a.numel() != b.numel():
+        raise ValueError("a and b must have the same number of elements")
+    if out is None:
+        raise ValueError("out is required (the call allocates nothing)")
+    _out(out, "out", torch.float32, 1)
+    _gpu(a=a, b=b, out=out)
+    with torch.cuda.device(a.device):
+        st = _lib.lib().residual_diff_noalloc(_ptr(a), _ptr(b), a.numel(), _ptr(out),
+                                              ctypes_ptr(_stream(a)))
+    _lib.check("residual_diff_noalloc", st)
     return out
 
 

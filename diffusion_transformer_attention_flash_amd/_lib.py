@@ -22,6 +22,7 @@ SIGNATURES = {
     "attn_fwd_accum": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P]),
     "attn_merge_into": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _P]),
     "residual_diff": (_I, [_P, _P, _I64, _P, _P, _P]),
+    "residual_diff_noalloc": (_I, [_P, _P, _I64, _P, _P]),
     "fbcache_step": (_I, [_P, _P, _I64, _F, _P, _P, _I64, _P, _P, _P, _P]),
     "fp8_quant_per_tensor": (_I, [_P, _I64, _P, _P, _P, _P]),
     "fp8_quant_per_tensor_multi": (_I, [_I, _P, _P, _P, _P, _P, _P]),

@@ -30,6 +30,7 @@
 // Both are bitwise reproducible.
 
 #include <algorithm>
+#include <mutex>
 
 #include "common.h"
 
@@ -343,11 +344,65 @@ static unsigned* ws_counter(void* ws) {
   return reinterpret_cast<unsigned*>(static_cast<char*>(ws) + kCounterOffset);
 }
 
+// residual_diff_noalloc's scratch: the same partials and counters as a
+// caller's workspace, in a file-scope device array (one copy per GPU, kept
+// until the process ends). It is zero when the library loads, and every call
+// returns its counters to zero. In host code `scratch` names a host-side
+// stand-in, never the device memory: kernels get the address that
+// hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[kWsBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+// Largest n of the scratch-backed entry point: the scratch holds the fixed
+// grid's partials whatever n is; this bound keeps the 64-bit chunk index
+// arithmetic exact.
+constexpr int64_t kNoAllocMaxN = (int64_t)1 << 62;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];
+
+// The device address of `scratch` on the current device, looked up once per
+// device with that device current.
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return DTA_ELAUNCH;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return DTA_ELAUNCH;
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return DTA_OK;
+}
+}  // namespace
+
 extern "C" int residual_diff(const void* a, const void* b, int64_t n, float* out,
                              void* ws, hipStream_t stream) {
   if (!a || !b || !out || !ws || n < 1) return DTA_EINVAL;
   if (!al16(a) || !al16(b) || !al16(ws) || (reinterpret_cast<uintptr_t>(out) & 3))
     return DTA_EALIGN;
+  hipLaunchKernelGGL(residual_diff_kernel<false>, dim3(kResBlocks), dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(a), static_cast<const uint16_t*>(b), n,
+                     static_cast<double*>(ws), ws_counter(ws), out, 0.0f, nullptr);
+  return hipGetLastError() == hipSuccess ? DTA_OK : DTA_ELAUNCH;
+}
+
+extern "C" int residual_diff_noalloc(const void* a, const void* b, int64_t n, float* out,
+                                     hipStream_t stream) {
+  if (!a || !b || !out || n < 1) return DTA_EINVAL;
+  if (n >= kNoAllocMaxN) return DTA_EINVAL;
+  if (!al16(a) || !al16(b) || (reinterpret_cast<uintptr_t>(out) & 3)) return DTA_EALIGN;
+  if (stream != nullptr) {
+    int dev = -1, cur = -1;
+    if (hipStreamGetDevice(stream, &dev) != hipSuccess || hipGetDevice(&cur) != hipSuccess)
+      return DTA_ELAUNCH;
+    if (dev != cur) return DTA_EINVAL;
+  }
+  void* ws = nullptr;
+  const int st = scratch_address(&ws);
+  if (st != DTA_OK) return st;
   hipLaunchKernelGGL(residual_diff_kernel<false>, dim3(kResBlocks), dim3(256), 0, stream,
                      static_cast<const uint16_t*>(a), static_cast<const uint16_t*>(b), n,
                      static_cast<double*>(ws), ws_counter(ws), out, 0.0f, nullptr);

@@ -153,6 +153,27 @@ int residual_diff(const void* a, const void* b, int64_t n, float* out,
                   void* ws, hipStream_t stream);
 
 /*
+ * residual_diff_noalloc -- residual_diff for callers that cannot allocate
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernel and the same result, bit for bit, with the
+ * workspace replaced by a scratch array inside the library. The call
+ * allocates nothing and frees nothing.
+ *
+ * The scratch is a fixed 20 736-byte device array per GPU, held until the
+ * process ends; it holds the fixed grid's 512 partial pairs and the arrival
+ * counters, so its size does not depend on n. Every call on one GPU shares
+ * it: calls that overlap on one GPU (two streams, or two host threads) race
+ * and must not be issued. Each call returns the counters to zero.
+ * a, b  bf16 [n], 16-byte aligned; 1 <= n < 2^62 (beyond that DTA_EINVAL)
+ * out   float, one device scalar, written
+ * stream  a stream of the current device (or 0); another device's stream
+ *         gives DTA_EINVAL. The first call on a device looks up the
+ *         scratch's address there (a failure gives DTA_ELAUNCH).
+ */
+int residual_diff_noalloc(const void* a, const void* b, int64_t n, float* out,
+                          hipStream_t stream);
+
+/*
  * fbcache_step -- First Block Cache's decision and cached-residual apply on
  * the device, with no host round trip (ParaAttention guide, section "First
  * Block Cache": when the first block's relative residual difference is small

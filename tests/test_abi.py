@@ -159,6 +159,13 @@ def test_layout_validation():
 
 def test_reductions_validation():
     lib = _lib.lib()
+    f = lib.residual_diff_noalloc
+    assert f(None, GOOD, 10, GOOD, None) == _lib.DTA_EINVAL
+    assert f(GOOD, GOOD, 10, None, None) == _lib.DTA_EINVAL
+    assert f(GOOD, GOOD, 0, GOOD, None) == _lib.DTA_EINVAL
+    assert f(GOOD, GOOD, 1 << 62, GOOD, None) == _lib.DTA_EINVAL      # beyond the limit
+    assert f(ODD, GOOD, 10, GOOD, None) == _lib.DTA_EALIGN
+    assert f(GOOD, GOOD, 10, ctypes.c_void_p(0x10002), None) == _lib.DTA_EALIGN
     assert lib.residual_diff(GOOD, GOOD, 0, GOOD, GOOD, None) == _lib.DTA_EINVAL
     assert lib.residual_diff(GOOD, GOOD, 10, GOOD, None, None) == _lib.DTA_EINVAL
     assert lib.residual_diff(ODD, GOOD, 10, GOOD, GOOD, None) == _lib.DTA_EALIGN
