@@ -165,18 +165,30 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_bf16_kernel(
     const uint16_t* kt = ks[buf];
     const uint16_t* vt = vs[buf];
 
-    // S^T = K . Q^T, BN keys x 32 queries.
+    // S^T = K . Q^T, BN keys x 32 queries. The K fragments of step ds+1 are
+    // read while the MFMAs of step ds run.
     f32x16 s[BN / 32];
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb) s[kb] = f32x16{};
+    bf16x8 kf[2][BN / 32];
 #pragma unroll
-    for (int ds = 0; ds < D / 16; ++ds)
+    for (int kb = 0; kb < BN / 32; ++kb)
+      kf[0][kb] = *reinterpret_cast<const bf16x8*>(kt + k_base + kb * 32 * C::kKS);
+    __builtin_amdgcn_sched_group_barrier(0x100, BN / 32, 0);
 #pragma unroll
-      for (int kb = 0; kb < BN / 32; ++kb) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-            kt + k_base + kb * 32 * C::kKS + ds * 16);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qr[ds], s[kb], 0, 0, 0);
+    for (int ds = 0; ds < D / 16; ++ds) {
+      if (ds + 1 < D / 16) {
+#pragma unroll
+        for (int kb = 0; kb < BN / 32; ++kb)
+          kf[(ds + 1) & 1][kb] = *reinterpret_cast<const bf16x8*>(
+              kt + k_base + kb * 32 * C::kKS + (ds + 1) * 16);
+        __builtin_amdgcn_sched_group_barrier(0x100, BN / 32, 0);
       }
+#pragma unroll
+      for (int kb = 0; kb < BN / 32; ++kb)
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ds & 1][kb], qr[ds], s[kb], 0, 0, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, BN / 32, 0);
+    }
 
     // Online softmax in the log2 domain.
     const int key_lim = Nkv - j * BN;
