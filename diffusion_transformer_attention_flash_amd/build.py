@@ -44,27 +44,43 @@ def _run(cmd):
     return r.stdout
 
 
-def build(verbose=False, jobs=4):
-    """Compile every csrc/*.hip source and link libdta.so; returns its path."""
+# The same library with a workgroup barrier at every point where the attention
+# kernels reuse LDS between phases (DTA_DEBUG_BARRIERS): its outputs must be
+# bit-identical to libdta.so's, which the GPU tests check.
+DEBUG_LIB_PATH = os.path.join(HERE, "libdta_debug.so")
+
+
+def build(verbose=False, jobs=4, lib_path=LIB_PATH, build_dir=BUILD_DIR, extra_flags=(),
+          link_flags=()):
+    """Compile every csrc/*.hip source and link a shared library (libdta.so
+    by default); returns its path."""
     hipcc = _hipcc()
-    os.makedirs(BUILD_DIR, exist_ok=True)
+    os.makedirs(build_dir, exist_ok=True)
     objs = []
     cmds = []
     for src in SOURCES:
-        obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
+        obj = os.path.join(build_dir, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmds.append([hipcc, *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([hipcc, *HIPCC_FLAGS, *extra_flags, "-c", os.path.join(CSRC, src), "-o", obj])
     with ThreadPoolExecutor(max_workers=max(1, int(jobs))) as ex:
         outs = list(ex.map(_run, cmds))
-    tmp = LIB_PATH + ".tmp"
-    outs.append(_run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]))
-    os.replace(tmp, LIB_PATH)
+    tmp = lib_path + ".tmp"
+    outs.append(_run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", *link_flags, *objs,
+                      "-o", tmp]))
+    os.replace(tmp, lib_path)
     if verbose:
         for o in outs:
             if o.strip():
                 print(o)
-    return LIB_PATH
+    return lib_path
+
+
+def build_debug_barriers(verbose=False, jobs=4):
+    """libdta_debug.so: DTA_DEBUG_BARRIERS builds of the same sources."""
+    return build(verbose, jobs, DEBUG_LIB_PATH, os.path.join(HERE, "_build_debug"),
+                 ("-DDTA_DEBUG_BARRIERS",))
 
 
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
+    print(build_debug_barriers(verbose="-v" in sys.argv))

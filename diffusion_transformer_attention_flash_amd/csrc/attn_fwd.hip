@@ -257,6 +257,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_bf16_kernel(
           oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb][t], oacc[db], 0, 0, 0);
         }
 
+    debug_sync();
     if (has_next) store_tile(buf ^ 1);
     __syncthreads();
   };
@@ -281,6 +282,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_bf16_kernel(
   const float lt = xhalf_sum(l_run);
   const int64_t li = (int64_t)bh * Nq + row;
   if constexpr (D == 128 && NW == 8) {
+    debug_sync();
     // O goes through LDS so that the global loads and stores of O are whole
     // 256-byte rows (16 lanes per row) instead of 16 bytes of each of 32
     // rows per instruction. The last tile's barrier has retired every K/V
@@ -322,6 +324,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_bf16_kernel(
         *reinterpret_cast<u32x4*>(stg + r * kPitch + ch * 16) = val;
       }
       wave_lds_sync();
+      debug_sync();
       // Two-part log-sum-exp merge in the log2 domain, as below.
       const float lc = m_run + log2f(lt);
       const float lr = row < Nq ? lse[li] * kLog2e : -INFINITY;
@@ -352,6 +355,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_bf16_kernel(
       if (g == 0 && row < Nq) lse[li] = (mm + log2f(den)) * kLn2;
     }
     wave_lds_sync();
+    debug_sync();
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
       const int r = 4 * kk + sub;

@@ -383,6 +383,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_fp8_kernel(
       qk_softmax(j, ks[buf], ves[buf], sk_e, pb, sb_e, mask_tag);
       pv(vs[buf], pb, sb_e);
     }
+    debug_sync();
     if (has_next) store_tile((buf + 1) % NBUF);
     __syncthreads();
   };
@@ -437,6 +438,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_fp8_kernel(
   else
     run(std::false_type{});
 
+  debug_sync();
   // MODE 0/1: l_run holds 108 l and O = s_v * acc / (108 l). MODE 2: l_run
   // holds l and O = acc / l (V's scale is in P).
   const float lt = xhalf_sum8(l_run);
@@ -463,6 +465,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_fp8_kernel(
       lse[(int64_t)bh * Nq + row] =
           (m_run + log2f(lt) - (MODE == 2 ? 0.0f : kLog2PScale)) * kLn2;
     wave_lds_sync();
+    debug_sync();
     // Store kk covers rows 4kk .. 4kk+3 of the wave; lane = 16 * (row % 4) + chunk.
     const int row0 = row - r_lo, sub = 2 * g + (r_lo >> 4), ch = r_lo & 15;
 #pragma unroll

@@ -57,6 +57,17 @@ __device__ __forceinline__ float wave_max(float x) {
   return x;
 }
 
+// The extra-barrier build (-DDTA_DEBUG_BARRIERS): a workgroup barrier at every
+// point where an attention kernel hands LDS from one phase to the next, on top
+// of the synchronisation the kernels rely on. Its outputs must not change.
+#ifndef DTA_DEBUG_BARRIERS
+#define DTA_DEBUG_BARRIERS 0
+#endif
+constexpr bool kDebugBarriers = DTA_DEBUG_BARRIERS != 0;
+__device__ __forceinline__ void debug_sync() {
+  if constexpr (kDebugBarriers) __syncthreads();
+}
+
 // Orders a wave's LDS writes before its later LDS reads of cells that other
 // lanes of the same wave wrote (wavefront scope: no s_barrier; LDS
 // instructions of one wave complete in order, so this only stops the
