@@ -4,6 +4,12 @@
         A plain device-to-device copy of known size (reads and writes MIB
         MiB each per launch): the reference that scales the FETCH_SIZE and
         WRITE_SIZE counters to bytes.
+    python bench_profile.py nkv-sweep [--nkv 1,64,...] [--reps 20]
+        bf16 attn_fwd at the FLUX query shape over a list of K/V lengths
+        (the fixed cost of a launch against its per-tile cost).
+    python bench_profile.py summarize-sweep DIR OUT.md --cmd "..."
+        Median duration per K/V length from that sweep's kernel trace and a
+        least-squares line fixed + per-tile.
     python bench_profile.py summarize-trace DIR OUT.md --cmd "..."
         Turns a `rocprofv3 --kernel-trace --stats -f csv` directory into a
         short markdown table (launches, average, median and total time per
@@ -43,6 +49,71 @@ def cmd_copy(args):
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes_read": n * 2, "copy_bytes_written": n * 2, "reps": args.reps}))
+
+
+SWEEP_NKV = (1, 64, 128, 256, 576, 1152, 2304, 4608)
+
+
+def _sweep_nkv(arg):
+    return [int(x) for x in arg.split(",")] if arg else list(SWEEP_NKV)
+
+
+def cmd_nkv_sweep(args):
+    """bf16 attn_fwd at the FLUX query shape (B=1, H=24, Nq=4608, D=128)
+    over a list of K/V lengths: for each, 3 warm-up launches then --reps
+    launches, in order, with a synchronisation between lengths (the order
+    summarize-sweep relies on)."""
+    import torch
+    sys.path.insert(0, ROOT)
+    import diffusion_transformer_attention_flash_amd as dta
+    import workloads
+    dev = torch.device("cuda", 0)
+    q, _, _ = workloads.make_qkv(2, 1, 24, 4608, 8, 128, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((1, 24, 4608), dtype=torch.float32, device=dev)
+    for nkv in _sweep_nkv(args.nkv):
+        _, k, v = workloads.make_qkv(2, 1, 24, 8, nkv, 128, device=dev)
+        torch.cuda.synchronize()
+        for _ in range(3 + args.reps):
+            dta.attn_fwd(q, k, v, 128 ** -0.5, o=o, lse=lse)
+        torch.cuda.synchronize()
+    print(json.dumps({"nkv": _sweep_nkv(args.nkv), "reps": args.reps}))
+
+
+def cmd_summarize_sweep(args):
+    """Median attn_fwd duration per K/V length from the nkv-sweep's kernel
+    trace, and the least-squares line time = fixed + per_tile * tiles
+    (tiles = ceil(Nkv / 64))."""
+    rows = []
+    for path in _find(args.dir, "kernel_trace.csv"):
+        with open(path) as f:
+            rows += [r for r in csv.DictReader(f) if "attn_fwd_bf16_kernel" in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    nkvs = _sweep_nkv(args.nkv)
+    per = 3 + args.reps
+    if len(rows) != per * len(nkvs):
+        raise SystemExit("expected %d attn_fwd launches, found %d" % (per * len(nkvs), len(rows)))
+    lines = ["# rocprofv3 kernel trace: %s" % args.title, "",
+             "Command (repo root): `%s`" % args.cmd, "",
+             "| Nkv | 64-key tiles | launches | median (us) | min (us) |", "|---:|---:|---:|---:|---:|"]
+    xs, ys = [], []
+    for i, nkv in enumerate(nkvs):
+        d = sorted(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+                   for r in rows[i * per + 3:(i + 1) * per])
+        med = d[len(d) // 2] / 1e3
+        tiles = -(-nkv // 64)
+        xs.append(tiles)
+        ys.append(med)
+        lines.append("| %d | %d | %d | %.2f | %.2f |" % (nkv, tiles, len(d), med, d[0] / 1e3))
+    n = len(xs)
+    mx, my = sum(xs) / n, sum(ys) / n
+    slope = sum((x - mx) * (y - my) for x, y in zip(xs, ys)) / sum((x - mx) ** 2 for x in xs)
+    fixed = my - slope * mx
+    lines += ["", "Least-squares line over all lengths: %.2f us fixed + %.3f us per 64-key tile "
+              "(432 workgroups of 256 query rows)." % (fixed, slope)]
+    with open(args.out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def _find(d, suffix):
@@ -260,6 +331,16 @@ def main():
     p = sub.add_parser("copy")
     p.add_argument("--mib", type=int, default=1024)
     p.add_argument("--reps", type=int, default=5)
+    p = sub.add_parser("nkv-sweep")
+    p.add_argument("--nkv", default="")
+    p.add_argument("--reps", type=int, default=20)
+    p = sub.add_parser("summarize-sweep")
+    p.add_argument("dir")
+    p.add_argument("out")
+    p.add_argument("--nkv", default="")
+    p.add_argument("--reps", type=int, default=20)
+    p.add_argument("--cmd", required=True)
+    p.add_argument("--title", default="")
     p = sub.add_parser("summarize-trace")
     p.add_argument("dir")
     p.add_argument("out")
@@ -280,6 +361,7 @@ def main():
     p.add_argument("--cmd", required=True)
     args = ap.parse_args()
     {"copy": cmd_copy, "summarize-trace": cmd_summarize_trace,
+     "nkv-sweep": cmd_nkv_sweep, "summarize-sweep": cmd_summarize_sweep,
      "summarize-pmc": cmd_summarize_pmc,
      "summarize-counters": cmd_summarize_counters}[args.cmd_name](args)
 
