@@ -10,6 +10,19 @@
     python bench_profile.py summarize-sweep DIR OUT.md --cmd "..."
         Median duration per K/V length from that sweep's kernel trace and a
         least-squares line fixed + per-tile.
+    python bench_profile.py balance-probe [--reps 20]
+        bf16 attn_fwd at four shapes of one kernel, interleaved: the FLUX
+        launch (432 workgroups, 72 K/V tiles each), its first round alone
+        (256 workgroups), its second round alone (176 workgroups), and the
+        same FLOPs spread evenly over 256 workgroups (121.5 tiles each), the
+        bound of any split-K schedule of the FLUX launch.
+    python bench_profile.py split-probe [--reps 20] [--sustained]
+        attn_fwd and attn_fwd_split interleaved at the FLUX launch and at
+        its second round alone (176 query tiles of 72 K/V tiles); with
+        --sustained, runs of 30 back-to-back launches of each, timed with
+        HIP events.
+    python bench_profile.py summarize-balance DIR OUT.md --cmd "..."
+        Median duration per shape from that probe's kernel trace.
     python bench_profile.py summarize-trace DIR OUT.md --cmd "..."
         Turns a `rocprofv3 --kernel-trace --stats -f csv` directory into a
         short markdown table (launches, average, median and total time per
@@ -78,6 +91,108 @@ def cmd_nkv_sweep(args):
             dta.attn_fwd(q, k, v, 128 ** -0.5, o=o, lse=lse)
         torch.cuda.synchronize()
     print(json.dumps({"nkv": _sweep_nkv(args.nkv), "reps": args.reps}))
+
+
+BALANCE_SHAPES = (
+    # (label, H, Nq, Nkv): B = 1, D = 128, 256 query rows per workgroup
+    ("FLUX launch: 432 workgroups x 72 tiles", 24, 4608, 4608),
+    ("first round alone: 256 x 72 tiles", 16, 4096, 4608),
+    ("second round alone: 176 x 72 tiles", 11, 4096, 4608),
+    ("equal FLOPs balanced: 256 x 121.5 tiles", 16, 4096, 7776),
+)
+
+
+def cmd_balance_probe(args):
+    """The shapes of BALANCE_SHAPES, launched in turn --reps times after 3
+    warm-up turns, so that clock drift falls on all of them alike."""
+    import torch
+    sys.path.insert(0, ROOT)
+    import diffusion_transformer_attention_flash_amd as dta
+    import workloads
+    dev = torch.device("cuda", 0)
+    cases = []
+    for _, h, nq, nkv in BALANCE_SHAPES:
+        q, _, _ = workloads.make_qkv(2, 1, h, nq, 8, 128, device=dev)
+        _, k, v = workloads.make_qkv(2, 1, h, 8, nkv, 128, device=dev)
+        o = torch.empty_like(q)
+        lse = torch.empty((1, h, nq), dtype=torch.float32, device=dev)
+        cases.append((q, k, v, o, lse))
+    torch.cuda.synchronize()
+    for _ in range(3 + args.reps):
+        for q, k, v, o, lse in cases:
+            dta.attn_fwd(q, k, v, 128 ** -0.5, o=o, lse=lse)
+    torch.cuda.synchronize()
+    print(json.dumps({"shapes": [c[0] for c in BALANCE_SHAPES], "reps": args.reps}))
+
+
+def cmd_split_probe(args):
+    import torch
+    sys.path.insert(0, ROOT)
+    import diffusion_transformer_attention_flash_amd as dta
+    import workloads
+    dev = torch.device("cuda", 0)
+    cases = []
+    for h in (24, 11):
+        nq = 4608 if h == 24 else 4096
+        q, _, _ = workloads.make_qkv(2, 1, h, nq, 8, 128, device=dev)
+        _, k, v = workloads.make_qkv(2, 1, h, 8, 4608, 128, device=dev)
+        cases.append((q, k, v, torch.empty_like(q),
+                      torch.empty((1, h, nq), dtype=torch.float32, device=dev)))
+    torch.cuda.synchronize()
+    if not args.sustained:
+        for _ in range(3 + args.reps):
+            for q, k, v, o, lse in cases:
+                dta.attn_fwd(q, k, v, 128 ** -0.5, o=o, lse=lse)
+                dta.attn_fwd_split(q, k, v, 128 ** -0.5, o=o, lse=lse)
+        torch.cuda.synchronize()
+        print(json.dumps({"reps": args.reps}))
+        return
+    # Sustained: 30 back-to-back launches of one variant per event pair, the
+    # variants alternating over 8 rounds; median per launch.
+    out = {}
+    for (q, k, v, o, lse), shape in zip(cases, ("FLUX 432 query tiles", "176 query tiles")):
+        times = {"attn_fwd": [], "attn_fwd_split": []}
+        for rnd in range(8):
+            for name in (("attn_fwd", "attn_fwd_split") if rnd % 2 == 0 else
+                         ("attn_fwd_split", "attn_fwd")):
+                fn = getattr(dta, name)
+                for _ in range(2):
+                    fn(q, k, v, 128 ** -0.5, o=o, lse=lse)
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                for _ in range(30):
+                    fn(q, k, v, 128 ** -0.5, o=o, lse=lse)
+                b.record()
+                torch.cuda.synchronize()
+                times[name].append(a.elapsed_time(b) / 30 * 1e3)
+        out[shape] = {n: round(statistics.median(t), 2) for n, t in times.items()}
+    print(json.dumps({"sustained_us_median": out}))
+
+
+def cmd_summarize_balance(args):
+    """Median attn_fwd duration per shape of the balance-probe's kernel trace
+    (launches cycle through BALANCE_SHAPES in order)."""
+    rows = []
+    for path in _find(args.dir, "kernel_trace.csv"):
+        with open(path) as f:
+            rows += [r for r in csv.DictReader(f) if "attn_fwd_bf16_kernel" in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    ns = len(BALANCE_SHAPES)
+    if len(rows) != ns * (3 + args.reps):
+        raise SystemExit("expected %d attn_fwd launches, found %d" % (ns * (3 + args.reps), len(rows)))
+    timed = rows[3 * ns:]
+    lines = ["# rocprofv3 kernel trace: %s" % args.title, "", args.cmd, "",
+             "| shape (B=1, D=128) | H | Nq | Nkv | launches | median (us) | min (us) | TFLOP/s at median |",
+             "|---|---:|---:|---:|---:|---:|---:|---:|"]
+    for i, (label, h, nq, nkv) in enumerate(BALANCE_SHAPES):
+        d = sorted(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in timed[i::ns])
+        med = d[len(d) // 2] / 1e3
+        flops = 4.0 * h * nq * nkv * 128
+        lines.append("| %s | %d | %d | %d | %d | %.2f | %.2f | %.1f |" % (
+            label, h, nq, nkv, len(d), med, d[0] / 1e3, flops / med / 1e6))
+    with open(args.out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def cmd_summarize_sweep(args):
@@ -334,6 +449,17 @@ def main():
     p = sub.add_parser("nkv-sweep")
     p.add_argument("--nkv", default="")
     p.add_argument("--reps", type=int, default=20)
+    p = sub.add_parser("balance-probe")
+    p.add_argument("--reps", type=int, default=20)
+    p = sub.add_parser("split-probe")
+    p.add_argument("--reps", type=int, default=20)
+    p.add_argument("--sustained", action="store_true")
+    p = sub.add_parser("summarize-balance")
+    p.add_argument("dir")
+    p.add_argument("out")
+    p.add_argument("--reps", type=int, default=20)
+    p.add_argument("--cmd", required=True)
+    p.add_argument("--title", default="")
     p = sub.add_parser("summarize-sweep")
     p.add_argument("dir")
     p.add_argument("out")
@@ -361,7 +487,9 @@ def main():
     p.add_argument("--cmd", required=True)
     args = ap.parse_args()
     {"copy": cmd_copy, "summarize-trace": cmd_summarize_trace,
-     "nkv-sweep": cmd_nkv_sweep, "summarize-sweep": cmd_summarize_sweep,
+     "nkv-sweep": cmd_nkv_sweep, "balance-probe": cmd_balance_probe,
+     "split-probe": cmd_split_probe,
+     "summarize-balance": cmd_summarize_balance, "summarize-sweep": cmd_summarize_sweep,
      "summarize-pmc": cmd_summarize_pmc,
      "summarize-counters": cmd_summarize_counters}[args.cmd_name](args)
 
