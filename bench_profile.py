@@ -16,11 +16,6 @@
         (256 workgroups), its second round alone (176 workgroups), and the
         same FLOPs spread evenly over 256 workgroups (121.5 tiles each), the
         bound of any split-K schedule of the FLUX launch.
-    python bench_profile.py split-probe [--reps 20] [--sustained]
-        attn_fwd and attn_fwd_split interleaved at the FLUX launch and at
-        its second round alone (176 query tiles of 72 K/V tiles); with
-        --sustained, runs of 30 back-to-back launches of each, timed with
-        HIP events.
     python bench_profile.py summarize-balance DIR OUT.md --cmd "..."
         Median duration per shape from that probe's kernel trace.
     python bench_profile.py summarize-trace DIR OUT.md --cmd "..."
@@ -123,50 +118,6 @@ def cmd_balance_probe(args):
             dta.attn_fwd(q, k, v, 128 ** -0.5, o=o, lse=lse)
     torch.cuda.synchronize()
     print(json.dumps({"shapes": [c[0] for c in BALANCE_SHAPES], "reps": args.reps}))
-
-
-def cmd_split_probe(args):
-    import torch
-    sys.path.insert(0, ROOT)
-    import diffusion_transformer_attention_flash_amd as dta
-    import workloads
-    dev = torch.device("cuda", 0)
-    cases = []
-    for h in (24, 11):
-        nq = 4608 if h == 24 else 4096
-        q, _, _ = workloads.make_qkv(2, 1, h, nq, 8, 128, device=dev)
-        _, k, v = workloads.make_qkv(2, 1, h, 8, 4608, 128, device=dev)
-        cases.append((q, k, v, torch.empty_like(q),
-                      torch.empty((1, h, nq), dtype=torch.float32, device=dev)))
-    torch.cuda.synchronize()
-    if not args.sustained:
-        for _ in range(3 + args.reps):
-            for q, k, v, o, lse in cases:
-                dta.attn_fwd(q, k, v, 128 ** -0.5, o=o, lse=lse)
-                dta.attn_fwd_split(q, k, v, 128 ** -0.5, o=o, lse=lse)
-        torch.cuda.synchronize()
-        print(json.dumps({"reps": args.reps}))
-        return
-    # Sustained: 30 back-to-back launches of one variant per event pair, the
-    # variants alternating over 8 rounds; median per launch.
-    out = {}
-    for (q, k, v, o, lse), shape in zip(cases, ("FLUX 432 query tiles", "176 query tiles")):
-        times = {"attn_fwd": [], "attn_fwd_split": []}
-        for rnd in range(8):
-            for name in (("attn_fwd", "attn_fwd_split") if rnd % 2 == 0 else
-                         ("attn_fwd_split", "attn_fwd")):
-                fn = getattr(dta, name)
-                for _ in range(2):
-                    fn(q, k, v, 128 ** -0.5, o=o, lse=lse)
-                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                a.record()
-                for _ in range(30):
-                    fn(q, k, v, 128 ** -0.5, o=o, lse=lse)
-                b.record()
-                torch.cuda.synchronize()
-                times[name].append(a.elapsed_time(b) / 30 * 1e3)
-        out[shape] = {n: round(statistics.median(t), 2) for n, t in times.items()}
-    print(json.dumps({"sustained_us_median": out}))
 
 
 def cmd_summarize_balance(args):
@@ -451,9 +402,6 @@ def main():
     p.add_argument("--reps", type=int, default=20)
     p = sub.add_parser("balance-probe")
     p.add_argument("--reps", type=int, default=20)
-    p = sub.add_parser("split-probe")
-    p.add_argument("--reps", type=int, default=20)
-    p.add_argument("--sustained", action="store_true")
     p = sub.add_parser("summarize-balance")
     p.add_argument("dir")
     p.add_argument("out")
@@ -488,7 +436,6 @@ def main():
     args = ap.parse_args()
     {"copy": cmd_copy, "summarize-trace": cmd_summarize_trace,
      "nkv-sweep": cmd_nkv_sweep, "balance-probe": cmd_balance_probe,
-     "split-probe": cmd_split_probe,
      "summarize-balance": cmd_summarize_balance, "summarize-sweep": cmd_summarize_sweep,
      "summarize-pmc": cmd_summarize_pmc,
      "summarize-counters": cmd_summarize_counters}[args.cmd_name](args)

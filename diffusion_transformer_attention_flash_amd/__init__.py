@@ -7,7 +7,6 @@ to the C ABI. Every step of the computation runs in the library's HIP
 kernels; there is no fallback path -- a missing library raises.
 
     attn_fwd(q, k, v, scale)              -> (o, lse)
-    attn_fwd_split(q, k, v, scale)        the same, a partial last round cut along K/V
     attn_merge(o_parts, lse_parts)        -> (o, lse)
     attn_fwd_accum(q, k, v, o, lse)       one ring step, merged into (o, lse)
     attn_merge_into(o, lse, o_part, lse_part)  pairwise in-place merge
@@ -21,9 +20,8 @@ kernels; there is no fallback path -- a missing library raises.
     fp8_quant_rows_pow2(x)                -> (x8 uint8, e8m0 uint8 per row)
     attn_fwd_fp8_rows / attn_fwd_fp8_rows_v   row-wise scaled fp8 attention
 
-The reductions share a small device workspace, attn_fwd_split a larger one;
-the binding keeps one of each per (device, stream), so calls on different
-streams never share them.
+The reductions share a small device workspace; the binding keeps one per
+(device, stream), so calls on different streams never share it.
 """
 
 import ctypes
@@ -33,7 +31,7 @@ import torch
 from . import _lib
 from ._lib import DtaError  # noqa: F401
 
-__all__ = ["attn_fwd", "attn_fwd_split", "split_workspace", "attn_merge", "attn_fwd_accum", "attn_merge_into", "residual_diff",
+__all__ = ["attn_fwd", "attn_merge", "attn_fwd_accum", "attn_merge_into", "residual_diff",
            "residual_diff_noalloc",
            "fbcache_step", "seq_concat", "seq_split", "head_concat", "head_split",
            "fp8_quant_rows_pow2", "attn_fwd_fp8_rows", "attn_fwd_fp8_rows_v",
@@ -41,7 +39,6 @@ __all__ = ["attn_fwd", "attn_fwd_split", "split_workspace", "attn_merge", "attn_
            "attn_fwd_fp8", "workspace", "DtaError"]
 
 _workspaces = {}
-_split_workspaces = {}
 
 
 def _stream(t):
@@ -111,32 +108,8 @@ def workspace(device):
     return ws
 
 
-def split_workspace(device):
-    """attn_fwd_split's workspace for ``device``'s current stream (allocated
-    and zero-filled once per (device, stream), as ``workspace``)."""
-    device = torch.device(device)
-    idx = device.index if device.index is not None else torch.cuda.current_device()
-    key = (idx, torch.cuda.current_stream(idx).cuda_stream)
-    ws = _split_workspaces.get(key)
-    if ws is None:
-        nbytes = int(_lib.lib().attn_fwd_split_ws_bytes())
-        ws = torch.zeros(nbytes, dtype=torch.uint8, device=torch.device("cuda", idx))
-        _split_workspaces[key] = ws
-    return ws
-
-
-def attn_fwd_split(q, k, v, scale=None, o=None, lse=None):
-    """attn_fwd with a partial last round of query tiles cut along K/V across
-    the idle compute units (same arguments and results)."""
-    return _attn_fwd("attn_fwd_split", q, k, v, scale, o, lse)
-
-
 def attn_fwd(q, k, v, scale=None, o=None, lse=None):
     """Non-causal attention: q [B,H,Nq,D], k/v [B,H,Nkv,D] bf16 -> (o bf16, lse f32)."""
-    return _attn_fwd("attn_fwd", q, k, v, scale, o, lse)
-
-
-def _attn_fwd(fn, q, k, v, scale, o, lse):
     _need(q, "q", torch.bfloat16, 4)
     _need(k, "k", torch.bfloat16, 4)
     _need(v, "v", torch.bfloat16, 4)
@@ -153,11 +126,9 @@ def _attn_fwd(fn, q, k, v, scale, o, lse):
         o = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
-    args = [_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nkv, D, float(scale)]
-    if fn == "attn_fwd_split":
-        args.append(_ptr(split_workspace(q.device)))
-    st = getattr(_lib.lib(), fn)(*args, ctypes_ptr(_stream(q)))
-    _lib.check(fn, st)
+    st = _lib.lib().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                             B, H, Nq, Nkv, D, float(scale), ctypes_ptr(_stream(q)))
+    _lib.check("attn_fwd", st)
     return o, lse
 
 

@@ -18,8 +18,6 @@ _I64 = ctypes.c_int64
 _F = ctypes.c_float
 SIGNATURES = {
     "attn_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P]),
-    "attn_fwd_split": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _P]),
-    "attn_fwd_split_ws_bytes": (ctypes.c_size_t, []),
     "attn_merge": (_I, [_P, _P, _I, _P, _P, _I, _I, _I, _I, _P]),
     "attn_fwd_accum": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P]),
     "attn_merge_into": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _P]),

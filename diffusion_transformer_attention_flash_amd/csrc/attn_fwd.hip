@@ -43,7 +43,6 @@
 // * Workgroup ids are remapped so that the workgroups of one XCD walk
 //   consecutive query tiles of the same head and share K/V through its L2.
 
-#include <algorithm>
 #include <type_traits>
 
 #include "common.h"
@@ -71,38 +70,6 @@ constexpr float kTau = 8.0f;
 // Fourth dword of a raw buffer resource (32-bit data format, no swizzle).
 constexpr int kBufDword3 = 0x00020000;
 
-// Split-K schedule of a last, partial round of workgroups (attn_fwd_split).
-// Items are query tiles of one (b, h), in (b, h)-major order. The first
-// n_full items run whole, one workgroup each. The K/V tiles of the remaining
-// items, laid end to end (units), are cut into n_wg contiguous ranges of
-// nearly equal length, one per further workgroup; a range is shorter than an
-// item, so it holds pieces of at most two items and an item is cut into at
-// most kMaxPieces pieces. A piece of a cut item leaves its unnormalised state
-// (the O accumulator, the reference max and the row sums, in the lanes'
-// register layout) in a slot of the workspace and counts in on the item's
-// counter; the piece that counts in last combines all pieces in piece order
-// (the same sums whichever piece that is) and writes O and LSE as usual.
-struct SplitArgs {
-  float* part;      // 2 slots per range workgroup
-  unsigned* cnt;    // one counter per cut item: zero before and after a call
-  int n_full;       // items run whole
-  int n_wg;         // workgroups sharing the remaining items
-  int units;        // remaining items * K/V tiles per item (< 2^31)
-};
-constexpr int kMaxPieces = 3;
-constexpr int kSplitMaxWg = 256;
-constexpr size_t kSplitCntBytes = 4096;
-static_assert(kSplitMaxWg * sizeof(unsigned) <= kSplitCntBytes, "split counters fit");
-
-// First unit of range w (w = n_wg gives the end).
-__device__ __forceinline__ int split_begin(int w, const SplitArgs& sa) {
-  return (int)((int64_t)w * sa.units / sa.n_wg);
-}
-// The range holding unit x: the largest w with split_begin(w) <= x.
-__device__ __forceinline__ int split_owner(int x, const SplitArgs& sa) {
-  return (int)((((int64_t)x + 1) * sa.n_wg - 1) / sa.units);
-}
-
 __device__ __forceinline__ float xhalf_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
                                                   false, false);
@@ -116,40 +83,19 @@ __device__ __forceinline__ float xhalf_sum(float x) {
 
 // ACCUM: instead of writing this K/V chunk's (O, LSE), merge it into the
 // running (O, LSE) already in o / lse (one ring-attention step, fused).
-// SPLIT: the schedule of SplitArgs (not with ACCUM).
-template <int D, int NW, int BN, bool ACCUM, bool SPLIT>
+template <int D, int NW, int BN, bool ACCUM>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
-    float* __restrict__ lse, int Nq, int Nkv, float c, int n_qt, SplitArgs sa_arg) {
-  static_assert(!(SPLIT && ACCUM), "split schedule writes O, it does not accumulate");
+    float* __restrict__ lse, int Nq, int Nkv, float c, int n_qt) {
   using C = AttnCfg<D, NW, BN>;
   __shared__ __attribute__((aligned(16))) uint16_t ks[2][BN * C::kKS];
   __shared__ __attribute__((aligned(16))) uint16_t vs[2][BN * C::kVS];
-  __shared__ bool s_last;   // SPLIT: this piece counted in last
-  // SPLIT: the schedule is read from LDS where it is used, so that it does
-  // not hold scalar registers through the K/V loop.
-  __shared__ uint32_t s_split[sizeof(SplitArgs) / 4];
-  auto split_args = [&]() {
-    uint32_t x[sizeof(SplitArgs) / 4];
-#pragma unroll
-    for (int i = 0; i < (int)(sizeof(SplitArgs) / 4); ++i)
-      x[i] = __builtin_amdgcn_readfirstlane(s_split[i]);
-    return __builtin_bit_cast(SplitArgs, x);
-  };
 
-  const int n_tiles = (Nkv + BN - 1) / BN;
-
-  // K/V tiles [tb, te) of query tile `blk`; w is the range workgroup's index
-  // under SPLIT (-1 for a whole item).
-  auto piece = [&](const int blk, const int tb, const int te) {
-  int tid = threadIdx.x;
-  // Under SPLIT a workgroup runs up to two pieces in a loop: an opaque copy
-  // of the thread id keeps the per-lane addressing inside the loop instead
-  // of being hoisted and held live across it.
-  if constexpr (SPLIT) asm volatile("" : "+v"(tid));
+  const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31;
+  const int blk = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = blk / n_qt, qt = blk - bh * n_qt;
   const int64_t q_base = (int64_t)bh * Nq * D;
   const uint16_t* kh = k + (int64_t)bh * Nkv * D;
@@ -205,7 +151,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_bf16_kernel(
   for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
 
-  load_tile(tb);
+  const int n_tiles = (Nkv + BN - 1) / BN;
+  load_tile(0);
   store_tile(0);
   __syncthreads();
 
@@ -213,7 +160,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_bf16_kernel(
   auto tile = [&](int j, auto buf_tag, auto mask_tag) {
     constexpr bool MASK = decltype(mask_tag)::value;
     constexpr int buf = decltype(buf_tag)::value;
-    const bool has_next = j + 1 < te;
+    const bool has_next = j + 1 < n_tiles;
     if (has_next) load_tile(j + 1);
     const uint16_t* kt = ks[buf];
     const uint16_t* vt = vs[buf];
@@ -317,108 +264,18 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_bf16_kernel(
 
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
-  const int n_full = (te == n_tiles && Nkv % BN != 0) ? te - 1 : te;
-  int j = tb;
+  const int n_full = (Nkv % BN == 0) ? n_tiles : n_tiles - 1;
+  int j = 0;
   for (; j + 1 < n_full; j += 2) {
     tile(j, B0{}, std::false_type{});
     tile(j + 1, B1{}, std::false_type{});
   }
   if (j < n_full) tile(j++, B0{}, std::false_type{});
-  if (j < te) {
-    if ((j - tb) & 1)
+  if (j < n_tiles) {
+    if (j & 1)
       tile(j, B1{}, std::true_type{});
     else
       tile(j, B0{}, std::true_type{});
-  }
-
-  if constexpr (SPLIT) {
-    const SplitArgs sa = split_args();
-    if ((int)blockIdx.x >= sa.n_full) {
-      const int w = xcd_remap(blockIdx.x - sa.n_full, sa.n_wg);
-      const int i0 = (blk - sa.n_full) * n_tiles;   // the item's first unit
-      const int w0 = split_owner(i0, sa);
-      const int np = split_owner(i0 + n_tiles - 1, sa) - w0 + 1;
-      if (np > 1) {
-        // Slot of piece kk: the item is the second piece of its first range
-        // when that range began in an earlier item, else the range's first.
-        auto slot = [&](int kk) -> float* {
-          const int wk = w0 + kk;
-          const int which = (kk == 0 && split_begin(wk, sa) < i0) ? 1 : 0;
-          return sa.part + (size_t)(2 * wk + which) * (C::kThreads * (D / 2 + 2)) + tid;
-        };
-        const int me = w - w0;
-        float* mine = slot(me);
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            __hip_atomic_store(mine + (db * 16 + r) * C::kThreads, oacc[db][r],
-                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(mine + (D / 2) * C::kThreads, m_run, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(mine + (D / 2 + 1) * C::kThreads, l_run, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-        // The slot is complete at device scope before the piece counts in:
-        // whoever counts in last then reads it.
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (tid == 0) {
-          unsigned* ctr = sa.cnt + (blk - sa.n_full);
-          const bool l = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED,
-                                                __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(np - 1);
-          if (l) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          s_last = l;
-        }
-        __syncthreads();
-        if (!s_last) return;
-        // Combine the pieces in piece order: weights 2^(m_k - M) against the
-        // largest reference max M, each sum started from zero by an fma.
-        const float* src[kMaxPieces];
-        float mk[kMaxPieces];
-        float mm = -INFINITY;
-#pragma unroll
-        for (int kk = 0; kk < kMaxPieces; ++kk) {
-          src[kk] = kk < np && kk != me ? slot(kk) : nullptr;
-          mk[kk] = kk >= np ? -INFINITY
-                   : kk == me ? m_run
-                   : __hip_atomic_load(src[kk] + (D / 2) * C::kThreads, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-          mm = fmaxf(mm, mk[kk]);
-        }
-        float wk[kMaxPieces];
-#pragma unroll
-        for (int kk = 0; kk < kMaxPieces; ++kk) wk[kk] = __builtin_amdgcn_exp2f(mk[kk] - mm);
-        float ls = 0.f;
-#pragma unroll
-        for (int kk = 0; kk < kMaxPieces; ++kk)
-          if (kk < np)
-            ls = fmaf(kk == me ? l_run
-                               : __hip_atomic_load(src[kk] + (D / 2 + 1) * C::kThreads,
-                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
-                      wk[kk], ls);
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          float t[kMaxPieces][16];
-#pragma unroll
-          for (int kk = 0; kk < kMaxPieces; ++kk)
-            if (kk < np && kk != me)
-#pragma unroll
-              for (int r = 0; r < 16; ++r)
-                t[kk][r] = __hip_atomic_load(src[kk] + (db * 16 + r) * C::kThreads,
-                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            float a = 0.f;
-#pragma unroll
-            for (int kk = 0; kk < kMaxPieces; ++kk)
-              if (kk < np) a = fmaf(kk == me ? oacc[db][r] : t[kk][r], wk[kk], a);
-            oacc[db][r] = a;
-          }
-        }
-        m_run = mm;
-        l_run = ls;
-      }
-    }
   }
 
   // Epilogue: lane owns query `row` and dims db*32 + 8*(r/4) + 4g + r%4.
@@ -558,36 +415,6 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_bf16_kernel(
       }
     if (g == 0) lse[li] = (mm + log2f(den)) * kLn2;
   }
-  };
-
-  if constexpr (!SPLIT) {
-    piece(xcd_remap(blockIdx.x, gridDim.x), 0, n_tiles);
-  } else {
-    if (threadIdx.x == 0) __builtin_memcpy(s_split, &sa_arg, sizeof(SplitArgs));
-    __syncthreads();
-    // A range workgroup runs the rest of one item, then (if its range goes
-    // on) the start of the next.
-    for (int second = 0; second < 2; ++second) {
-      const SplitArgs sa = split_args();
-      int blk, tb = 0, te = n_tiles;
-      if ((int)blockIdx.x < sa.n_full) {
-        if (second) return;
-        blk = xcd_remap(blockIdx.x, sa.n_full);
-      } else {
-        // Ranges of neighbouring w run on one XCD (see xcd_remap).
-        const int w = xcd_remap(blockIdx.x - sa.n_full, sa.n_wg);
-        const int u0 = split_begin(w, sa), u1 = split_begin(w + 1, sa);
-        const int it = u0 / n_tiles + second;   // tail item of this piece
-        const int lo = max(u0, it * n_tiles), hi = min(u1, (it + 1) * n_tiles);
-        if (lo >= hi) return;
-        blk = sa.n_full + it;
-        tb = lo - it * n_tiles;
-        te = hi - it * n_tiles;
-        if (second) __syncthreads();   // the second piece restages the K/V buffers
-      }
-      piece(blk, tb, te);
-    }
-  }
 }
 
 template <int D, int NW, int BN, bool ACCUM>
@@ -598,74 +425,12 @@ static int launch_attn_fwd(const void* q, const void* k, const void* v,
   const int n_qt = (Nq + C::kBM - 1) / C::kBM;
   const int64_t grid = (int64_t)n_qt * B * H;
   if (grid > 0x7FFFFFFF) return DTA_EUNSUPPORTED;
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, NW, BN, ACCUM, false>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, NW, BN, ACCUM>), dim3((unsigned)grid),
                      dim3(C::kThreads), 0, stream,
                      static_cast<const uint16_t*>(q),
                      static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o),
-                     lse, Nq, Nkv, scale * kLog2e, n_qt, SplitArgs{});
-  return hipGetLastError() == hipSuccess ? DTA_OK : DTA_ELAUNCH;
-}
-
-// Split-K workspace: the cut items' counters, then 2 slots per range
-// workgroup, each the 8-wave D = 128 workgroup's registers (64 O values, the
-// reference max and the row sum per lane).
-constexpr size_t kSplitSlotBytes = (size_t)512 * (128 / 2 + 2) * sizeof(float);
-constexpr size_t kSplitWsBytes = kSplitCntBytes + 2 * kSplitMaxWg * kSplitSlotBytes;
-// Shortest range worth cutting for, in K/V tiles.
-constexpr int kSplitMinTiles = 16;
-
-// Compute units of the stream's device (cached per device).
-static int stream_cu_count(hipStream_t stream) {
-  static int cache[64];
-  int dev = 0;
-  if ((stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev)) != hipSuccess ||
-      dev < 0 || dev >= 64)
-    return 0;
-  if (cache[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-      return 0;
-    cache[dev] = n;
-  }
-  return cache[dev];
-}
-
-// The D = 128 launch under the split-K schedule when the last round of
-// workgroups is partial and its ranges are long enough; else the plain launch.
-static int launch_attn_fwd_split(const void* q, const void* k, const void* v, void* o,
-                                 float* lse, int B, int H, int Nq, int Nkv, float scale,
-                                 void* ws, hipStream_t stream) {
-  using C = AttnCfg<128, 8, 64>;
-  const int n_qt = (Nq + C::kBM - 1) / C::kBM;
-  const int64_t n_items = (int64_t)n_qt * B * H;
-  if (n_items > 0x7FFFFFFF) return DTA_EUNSUPPORTED;
-  const int n_tiles = (Nkv + 63) / 64;
-  const int n_cu = std::min(stream_cu_count(stream), kSplitMaxWg);
-  const int64_t tail = n_cu > 0 ? n_items % n_cu : 0;
-  SplitArgs sa{};
-  if (tail > 0) {
-    // Fewer than half a round left: two pieces per item.
-    sa.n_wg = (int)std::min<int64_t>(n_cu, 2 * tail);
-    const int64_t units = tail * n_tiles;
-    const int64_t lmin = units / sa.n_wg;
-    if (units < 0x7FFFFFFF && lmin >= kSplitMinTiles &&
-        (n_tiles - 1 + lmin - 1) / lmin + 1 <= kMaxPieces) {
-      sa.units = (int)units;
-      sa.n_full = (int)(n_items - tail);
-      sa.cnt = static_cast<unsigned*>(ws);
-      sa.part = reinterpret_cast<float*>(static_cast<char*>(ws) + kSplitCntBytes);
-    } else {
-      sa.n_wg = 0;
-    }
-  }
-  if (sa.n_wg == 0)
-    return launch_attn_fwd<128, 8, 64, false>(q, k, v, o, lse, B, H, Nq, Nkv, scale, stream);
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, 8, 64, false, true>),
-                     dim3((unsigned)(sa.n_full + sa.n_wg)), dim3(C::kThreads), 0, stream,
-                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                     static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, Nq,
-                     Nkv, scale * kLog2e, n_qt, sa);
+                     lse, Nq, Nkv, scale * kLog2e, n_qt);
   return hipGetLastError() == hipSuccess ? DTA_OK : DTA_ELAUNCH;
 }
 
@@ -698,20 +463,6 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o,
   if (st != DTA_OK) return st;
   if (D == 128)
     return launch_attn_fwd<128, 8, 64, false>(q, k, v, o, lse, B, H, Nq, Nkv, scale, stream);
-  return launch_attn_fwd<64, 4, 64, false>(q, k, v, o, lse, B, H, Nq, Nkv, scale, stream);
-}
-
-extern "C" size_t attn_fwd_split_ws_bytes(void) { return kSplitWsBytes; }
-
-extern "C" int attn_fwd_split(const void* q, const void* k, const void* v, void* o,
-                              float* lse, int B, int H, int Nq, int Nkv, int D, float scale,
-                              void* ws, hipStream_t stream) {
-  const int st = check_attn_args(q, k, v, o, lse, B, H, Nq, Nkv, D, scale);
-  if (st != DTA_OK) return st;
-  if (!ws) return DTA_EINVAL;
-  if (!aligned(ws, 16)) return DTA_EALIGN;
-  if (D == 128)
-    return launch_attn_fwd_split(q, k, v, o, lse, B, H, Nq, Nkv, scale, ws, stream);
   return launch_attn_fwd<64, 4, 64, false>(q, k, v, o, lse, B, H, Nq, Nkv, scale, stream);
 }
 

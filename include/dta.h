@@ -65,37 +65,6 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              hipStream_t stream);
 
 /*
- * attn_fwd_split -- attn_fwd, with the K/V loop of a last, partial round of
- * workgroups cut across the compute units that round would leave idle
- * (split-K). Same operation, arguments and outputs as attn_fwd; the sums of a
- * cut row are regrouped by the exact log-sum-exp identity of attn_merge
- * (diffusers "Context parallelism" guide, section "Ring Attention").
- *
- * With D = 128 a workgroup holds 256 query rows of one (b, h) and fills one
- * compute unit. With C = min(compute units of the stream's device, 256) and
- * n = B * H * ceil(Nq / 256) query tiles, the first n - (n mod C) tiles run
- * whole; the K/V tiles (64 keys) of the other r = n mod C query tiles are
- * laid end to end and cut into min(C, 2r) contiguous ranges of nearly equal
- * length, one workgroup each. The pieces of a cut query tile leave float32
- * partial sums in ws; the last piece to finish combines them in piece order
- * (results do not depend on timing: bitwise reproducible) and writes O and
- * LSE. They differ from attn_fwd's by float32 rounding of those rows' sums.
- * When r = 0, when a range would hold fewer than 16 K/V tiles, or for D = 64,
- * the call is attn_fwd.
- *
- * ws   device workspace of attn_fwd_split_ws_bytes() bytes, 16-byte aligned,
- *      zero-filled once before first use (the call leaves its counters zero);
- *      calls that share ws must not run concurrently
- * Returns as attn_fwd; DTA_EINVAL also for ws == NULL.
- */
-int attn_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse,
-                   int B, int H, int Nq, int Nkv, int D, float scale, void* ws,
-                   hipStream_t stream);
-
-/* Bytes of attn_fwd_split's workspace (about 66 MiB). */
-size_t attn_fwd_split_ws_bytes(void);
-
-/*
  * attn_merge -- combine partial (O_p, LSE_p), p = 0..n_parts-1, computed by
  * attn_fwd over disjoint K/V chunks, into attention over their union:
  *     M = max_p LSE_p;  w_p = exp(LSE_p - M);  W = sum_p w_p

@@ -55,22 +55,6 @@ def test_attn_fwd_validation():
     assert f(GOOD, GOOD, GOOD, GOOD, ctypes.c_void_p(0x10002), 1, 1, 1, 1, 64, 0.1, None) == _lib.DTA_EALIGN
 
 
-def test_attn_fwd_split_validation():
-    lib = _lib.lib()
-    f = lib.attn_fwd_split
-    ok = (GOOD, GOOD, GOOD, GOOD, GOOD)
-    # ws covers the counters and two slots of 256 x 128 float32 values (plus
-    # a max and a sum per lane) for each of up to 256 range workgroups
-    assert lib.attn_fwd_split_ws_bytes() >= 2 * 256 * 512 * 66 * 4
-    assert f(*ok, 1, 1, 1, 1, 128, 0.1, None, None) == _lib.DTA_EINVAL     # no workspace
-    assert f(*ok, 1, 1, 1, 1, 128, 0.1, ODD, None) == _lib.DTA_EALIGN
-    assert f(None, GOOD, GOOD, GOOD, GOOD, 1, 1, 1, 1, 128, 0.1, GOOD, None) == _lib.DTA_EINVAL
-    assert f(*ok, 1, 1, 1, 0, 128, 0.1, GOOD, None) == _lib.DTA_EINVAL
-    assert f(*ok, 1, 1, 1, 1, 96, 0.1, GOOD, None) == _lib.DTA_EUNSUPPORTED
-    assert f(*ok, 1, 1, 1, 1, 128, float("nan"), GOOD, None) == _lib.DTA_EINVAL
-    assert f(ODD, GOOD, GOOD, GOOD, GOOD, 1, 1, 1, 1, 128, 0.1, GOOD, None) == _lib.DTA_EALIGN
-
-
 def test_attn_fwd_fp8_validation():
     f = _lib.lib().attn_fwd_fp8
     assert f(GOOD, GOOD, GOOD, None, GOOD, GOOD, 1, 1, 1, 1, 128, 0.1, None) == _lib.DTA_EINVAL
