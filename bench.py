@@ -317,7 +317,7 @@ def cpu_baseline(dev, scale):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--video-reps", type=int, default=5)
     ap.add_argument("--no-video", action="store_true")
