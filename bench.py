@@ -219,7 +219,7 @@ def cpu_baseline(dev, scale):
         r = fn()
         return r, time.perf_counter() - t0
 
-    # C1: the tiny case, all rows, plus its 4-chunk merge.
+    # The tiny case (B=1, H=2, N=256, D=64), all rows, plus its 4-chunk merge.
     c = workloads.CONFIGS["tiny"]
     q, k, v = workloads.workload_qkv("tiny")
     sc = c["D"] ** -0.5
@@ -229,9 +229,9 @@ def cpu_baseline(dev, scale):
         parts = [oracle.attention(q, kc, vc, sc) for kc, vc in workloads.split_kv(k, v, c["chunks"])]
         oracle.merge(np.stack([p[0] for p in parts]), np.stack([p[1] for p in parts]))
     _, dt = timed(c1)
-    out["c1_tiny"] = {"s": dt, "sample": "all 2x256 rows, plus the 4x64-key chunked merge"}
+    out["tiny_256"] = {"s": dt, "sample": "all 2x256 rows, plus the 4x64-key chunked merge"}
 
-    # C2: FLUX bf16, whole heads, as many as fit in ~8 s.
+    # FLUX 1024^2 bf16 (H=24, N=4608, D=128), whole heads, as many as fit in ~8 s.
     c = workloads.CONFIGS["flux_1024"]
     q, k, v = workloads.workload_qkv("flux_1024")
     B, H, N, D = c["B"], c["H"], c["N"], c["D"]
@@ -242,11 +242,11 @@ def cpu_baseline(dev, scale):
         if time.perf_counter() - t0 > 8.0:
             break
     dt = time.perf_counter() - t0
-    c2_tflops = attn_flop(B, done, N, N, D) / dt / 1e12
-    out["c2_flux_1024"] = {"s": dt, "heads": done, "TFLOP/s": c2_tflops,
+    flux_tflops = attn_flop(B, done, N, N, D) / dt / 1e12
+    out["flux_1024"] = {"s": dt, "heads": done, "TFLOP/s": flux_tflops,
                            "sample": "%d of %d heads, all %d rows each" % (done, H, N)}
 
-    # C3: the 8 uneven chunks and their merge, head by head, as many heads
+    # The FLUX K/V in 8 uneven chunks and their merge, head by head, as many heads
     # as fit in ~8 s.
     c3 = workloads.CONFIGS["flux_1024_chunked"]
     lens = workloads.chunk_lengths(c3["config"], N, c3["n_chunks"], c3["min_chunk"])
@@ -260,12 +260,12 @@ def cpu_baseline(dev, scale):
         if time.perf_counter() - t0 > 8.0:
             break
     dt = time.perf_counter() - t0
-    out["c3_flux_8_chunks"] = {"s": dt, "heads": done,
+    out["flux_1024_8_chunks"] = {"s": dt, "heads": done,
                                "TFLOP/s": attn_flop(B, done, N, N, D) / dt / 1e12,
                                "sample": "%d of %d heads: 8 chunk attentions %s + merge"
                                          % (done, H, lens)}
 
-    # C4: the video shape, 256 rows per head (generated on the GPU as the
+    # The 119 056-token video shape, 256 rows per head (generated on the GPU as the
     # tests do, copied back head by head), for as many heads as fit in ~8 s.
     cv = workloads.CONFIGS["hunyuan_720p_129f"]
     qv, kv, vv = workloads.workload_qkv("hunyuan_720p_129f", device=dev)
@@ -285,14 +285,14 @@ def cpu_baseline(dev, scale):
     del qv, kv, vv
     nv = cv["N"]
     flop_rows = attn_flop(1, done, rows.shape[1], nv, cv["D"])
-    out["c4_video"] = {"s": busy, "heads": done, "TFLOP/s": flop_rows / busy / 1e12,
+    out["hunyuan_720p_129f"] = {"s": busy, "heads": done, "TFLOP/s": flop_rows / busy / 1e12,
                        "sample": "%d rows per head x %d of %d heads against all %d keys "
                                  "(oracle time only, not the host copies)"
                                  % (rows.shape[1], done, cv["H"], nv),
                        "extrapolated_full_tensor_s": busy * (nv / rows.shape[1]) * (cv["H"] / done),
                        "extrapolation": "x(119056/256 rows) x(24/heads): labelled estimate"}
 
-    # C5: the fp8 oracle on the FLUX tensors (per-tensor quantisation of the
+    # The fp8 oracle on the FLUX tensors (per-tensor quantisation of the
     # whole Q, K and V, then attention head by head, as many heads as fit in
     # ~8 s), and the fp64 residual sum over the whole [1, 4608, 3072] pair.
     c5 = workloads.CONFIGS["flux_1024_fp8"]
@@ -309,7 +309,7 @@ def cpu_baseline(dev, scale):
     ra, rb = workloads.residual_pair(c5["config"], c5["residual_shape"], c5["residual_noise"])
     (_, dt_r) = timed(lambda: oracle.residual_diff(ra, rb))
     res_bytes = 2 * ra.numel() * 2
-    out["c5_fp8_and_residual"] = {
+    out["flux_1024_fp8_and_residual"] = {
         "quantise_s": dt_q, "fp8_attention_s": dt, "heads": done,
         "fp8_TFLOP/s": attn_flop(B, done, N, N, D) / dt / 1e12,
         "residual_s": dt_r, "residual_GB/s": res_bytes / dt_r / 1e9,
@@ -318,12 +318,12 @@ def cpu_baseline(dev, scale):
                   % (done, H, ra.numel())}
     info = cpu_info()
     return {
-        "value": c2_tflops,
+        "value": flux_tflops,
         "unit": "TFLOP/s",
         "cores": info["blas_threads"] or info["cores_available"],
         "kind": "oracle",
         "sample": "float64 numpy oracle.attention on %s of the FLUX 4608-token shape; "
-                  "the other configurations in 'configs'" % out["c2_flux_1024"]["sample"],
+                  "the other configurations in 'configs'" % out["flux_1024"]["sample"],
         "configs": out,
         **info,
     }
