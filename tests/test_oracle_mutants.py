@@ -10,6 +10,7 @@ CPU only), at least one of the pins that cover that function must fail; with
 the real oracle every one of them passes.
 """
 
+import importlib
 import math
 
 import numpy as np
@@ -224,6 +225,108 @@ def q_coarse_subnormals(x):
     return np.where(sub, np.round(x / 2.0 ** -8) * 2.0 ** -8, RND(x))
 
 
+# ---- layout ---------------------------------------------------------------
+
+SEQ_SPLIT, SEQ_CONCAT = oracle.layout.seq_split, oracle.layout.seq_concat
+HEAD_SPLIT, HEAD_CONCAT = oracle.layout.head_split, oracle.layout.head_concat
+
+
+def l_split_one_late(x, lens, padded=None):
+    x = np.asarray(x)
+    return SEQ_SPLIT(np.roll(x, -1, axis=2), lens, padded)
+
+
+def l_concat_reversed(parts, lens):
+    return SEQ_CONCAT(list(parts)[::-1], list(lens)[::-1])
+
+
+def l_padding_not_zero(x, lens, padded=None):
+    out = SEQ_SPLIT(x, lens, padded)
+    for part, n in zip(out, lens):
+        part[:, :, n:] = 1
+    return out
+
+
+def l_head_cuts_off_by_one(x, heads):
+    heads = list(heads)
+    if len(heads) > 1 and heads[0] > 1:
+        heads = [heads[0] - 1] + heads[1:-1] + [heads[-1] + 1]
+    return HEAD_SPLIT(x, heads)
+
+
+def l_head_concat_reversed(parts):
+    return HEAD_CONCAT(list(parts)[::-1])
+
+
+# ---- FBCache step -----------------------------------------------------------
+
+FBC = oracle.fbcache_step
+
+
+def f_not_strict(r, r_prev, threshold, hidden, cached):
+    diff, use, out = FBC(r, r_prev, threshold, hidden, cached)
+    if np.float32(diff) == np.float32(threshold):
+        use = True
+        out = FBC(r, r_prev, np.inf, hidden, cached)[2]
+    return diff, use, out
+
+
+def f_decided_in_float64(r, r_prev, threshold, hidden, cached):
+    diff, _, _ = FBC(r, r_prev, threshold, hidden, cached)
+    use = bool(diff < threshold)
+    return diff, use, FBC(r, r_prev, np.inf if use else -np.inf, hidden, cached)[2]
+
+
+def f_nan_reuses(r, r_prev, threshold, hidden, cached):
+    diff, use, out = FBC(r, r_prev, threshold, hidden, cached)
+    if np.isnan(diff):
+        use = True
+        out = FBC(r, r_prev, np.inf, hidden, cached)[2]
+    return diff, use, out
+
+
+def f_sum_not_rounded(r, r_prev, threshold, hidden, cached):
+    diff, use, out = FBC(r, r_prev, threshold, hidden, cached)
+    if use:
+        out = _f64(hidden).reshape(np.shape(out)) + _f64(cached).reshape(np.shape(out))
+    return diff, use, out
+
+
+def b_truncates(x):
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)
+    return np.where(np.isfinite(x), np.ldexp(np.trunc(m * 256.0) / 256.0, e), x)
+
+
+# ---- row-wise fp8 -----------------------------------------------------------
+
+POW2, PBLOCK = oracle.pow2_exponent, oracle.p_block_exponents
+
+
+def p_exponent_one_high(amax):
+    e = POW2(amax)
+    return np.where(np.asarray(amax) == 0, e, e + 1)
+
+
+def p_exponent_boundary(amax):
+    amax = np.asarray(amax, dtype=np.float64)
+    m, k = np.frexp(amax)
+    e = np.where(m < 0.875, k - 9, k - 8)
+    return np.where(amax == 0, 0, np.clip(e, -127, 127)).astype(np.int64)
+
+
+def p_blocks_share_the_row_max(pv, blocks):
+    e = PBLOCK(pv, blocks)
+    return np.broadcast_to(e.max(axis=1, keepdims=True), e.shape).copy()
+
+
+def p_blocks_take_the_min(pv, blocks):
+    pv = np.asarray(pv, dtype=np.float64)
+    blocks = np.asarray(blocks)
+    starts = np.flatnonzero(np.r_[True, blocks[1:] != blocks[:-1]])
+    return POW2(np.minimum.reduceat(pv, starts, axis=1))
+
+
 # ---- which pins cover which function ---------------------------------------
 
 ATTN_PINS = [
@@ -265,7 +368,35 @@ FP8_PINS = [
     pins.test_fp8_attention_exact_power_of_two_probabilities,
 ]
 
-# (name patched in ``oracle`` and, where the oracle calls it internally, in
+LAYOUT_PINS = [
+    pins.test_layout_seq_split_positions_by_formula,
+    pins.test_layout_head_split_positions_by_formula,
+    pins.test_layout_ulysses_round_trip_matches_global_slicing,
+    pins.test_layout_ring_anything_pad_gather_trim,
+]
+FBCACHE_PINS = [
+    pins.test_fbcache_bf16_round_matches_torch_from_float32,
+    pins.test_fbcache_sum_is_correctly_rounded,
+    pins.test_fbcache_decision_closed_forms,
+    pins.test_fbcache_apply_rounds_the_sum_once_to_bf16,
+    pins.test_fbcache_decision_is_taken_in_float32,
+]
+ROWS_PINS = [
+    pins.test_rows_pow2_exponent_is_minimal,
+    pins.test_rows_pow2_codes_match_torch_and_error_bound,
+    pins.test_rows_pow2_attention_beats_per_tensor_on_outlier_tokens,
+    lambda: pins.test_p_block_partition(32),
+    pins.test_p_block_exponent_is_minimal_and_codes_match_torch,
+    pins.test_rows_v_uniform_scores_give_the_mean_of_v,
+    pins.test_rows_v_beats_per_tensor_v_on_an_outlier_value_token,
+    pins.test_rows_v_keeps_a_diffuse_tail_that_x448_p_scaling_flushes,
+    pins.test_rows_v_block_size_closed_form_uniform_scores,
+    lambda: pins.test_rows_v_exact_power_of_two_probabilities(1),
+    lambda: pins.test_rows_v_exact_power_of_two_probabilities(64),
+]
+
+# (name patched in ``oracle`` -- or in ``oracle.layout`` / ``oracle.residual``
+# for a dotted name -- and, where the oracle calls it internally, in
 # ``oracle.fp8``; the mutant; the pins that cover it)
 MUTANTS = {
     "attention: scale dropped": ("attention", a_scale_dropped, ATTN_PINS),
@@ -299,6 +430,25 @@ MUTANTS = {
     "e4m3 round: ties away from zero": ("e4m3_round", q_ties_away, FP8_PINS),
     "e4m3 round: no saturation": ("e4m3_round", q_no_saturation, FP8_PINS),
     "e4m3 round: subnormal spacing 2^-8": ("e4m3_round", q_coarse_subnormals, FP8_PINS),
+    "layout: split parts one token late": ("layout.seq_split", l_split_one_late, LAYOUT_PINS),
+    "layout: concat in reverse part order": ("layout.seq_concat", l_concat_reversed,
+                                             LAYOUT_PINS),
+    "layout: padding rows not zero": ("layout.seq_split", l_padding_not_zero, LAYOUT_PINS),
+    "layout: head cuts off by one": ("layout.head_split", l_head_cuts_off_by_one, LAYOUT_PINS),
+    "layout: head concat in reverse part order": ("layout.head_concat", l_head_concat_reversed,
+                                                  LAYOUT_PINS),
+    "fbcache: reuse at diff == threshold": ("fbcache_step", f_not_strict, FBCACHE_PINS),
+    "fbcache: decision in float64": ("fbcache_step", f_decided_in_float64, FBCACHE_PINS),
+    "fbcache: NaN diff reuses": ("fbcache_step", f_nan_reuses, FBCACHE_PINS),
+    "fbcache: sum not rounded to bf16": ("fbcache_step", f_sum_not_rounded, FBCACHE_PINS),
+    "fbcache: bf16 rounding truncates": ("residual._bf16_round", b_truncates, FBCACHE_PINS),
+    "rows: exponent one too high": ("pow2_exponent", p_exponent_one_high, ROWS_PINS),
+    "rows: exponent boundary at 448 exclusive": ("pow2_exponent", p_exponent_boundary,
+                                                 ROWS_PINS),
+    "rows: P blocks share the row maximum": ("p_block_exponents", p_blocks_share_the_row_max,
+                                             ROWS_PINS),
+    "rows: P block exponent from the block minimum": ("p_block_exponents",
+                                                      p_blocks_take_the_min, ROWS_PINS),
 }
 
 
@@ -317,13 +467,20 @@ def _failures(pin_list):
 
 
 def _patch(monkeypatch, name, fn):
+    if "." in name:
+        mod, attr = name.split(".")
+        monkeypatch.setattr(getattr(oracle, mod) if mod == "layout" else
+                            importlib.import_module("oracle." + mod), attr, fn)
+        return
     monkeypatch.setattr(oracle, name, fn)
     if hasattr(ofp8, name):
         monkeypatch.setattr(ofp8, name, fn)
 
 
-@pytest.mark.parametrize("pin_list", [ATTN_PINS, MERGE_PINS, RESID_PINS, FP8_PINS],
-                         ids=["attention", "merge", "residual", "fp8"])
+@pytest.mark.parametrize("pin_list", [ATTN_PINS, MERGE_PINS, RESID_PINS, FP8_PINS, LAYOUT_PINS,
+                                      FBCACHE_PINS, ROWS_PINS],
+                         ids=["attention", "merge", "residual", "fp8", "layout", "fbcache",
+                              "rows"])
 def test_pins_pass_on_the_real_oracle(pin_list):
     assert _failures(pin_list) == 0
 

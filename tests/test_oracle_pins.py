@@ -500,6 +500,20 @@ def test_fbcache_decision_closed_forms():
     assert oracle.fbcache_step(z, z, 1e30, h, c)[1] is False       # 0 / 0 = NaN
 
 
+def test_fbcache_apply_rounds_the_sum_once_to_bf16():
+    # hidden + cached of random bf16 values: the float32 sum of two bf16
+    # values is exact here, and torch's float32 -> bfloat16 cast (round to
+    # nearest even) is the reference; most sums need that rounding.
+    g = torch.Generator().manual_seed(11)
+    h = (torch.randn(4096, generator=g) * 3).to(torch.bfloat16)
+    c = (torch.randn(4096, generator=g) * 0.01).to(torch.bfloat16)
+    _, use, out = oracle.fbcache_step(h, h, 0.5, h, c)            # diff 0: reuse
+    ref = (h.to(torch.float32) + c.to(torch.float32)).to(torch.bfloat16).to(torch.float64)
+    assert use is True
+    np.testing.assert_array_equal(out, ref.numpy())
+    assert not np.array_equal(out, (h.double() + c.double()).numpy())   # rounding mattered
+
+
 def test_fbcache_decision_is_taken_in_float32():
     # diff = 1/3 in float64; float32(1/3) = 0.3333333432674408 > 1/3
     b = torch.tensor([3.0]).to(torch.bfloat16)
