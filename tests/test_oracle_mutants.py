@@ -18,6 +18,7 @@ import pytest
 
 import oracle
 import oracle.fp8 as ofp8
+import test_fp8_bound as fp8_bound
 import test_oracle_pins as pins
 
 ATTN, MERGE, RESID = oracle.attention, oracle.merge, oracle.residual_diff
@@ -327,6 +328,46 @@ def p_blocks_take_the_min(pv, blocks):
     return POW2(np.minimum.reduceat(pv, starts, axis=1))
 
 
+# ---- per-tensor fp8 attention ------------------------------------------------
+
+def _p8_attention(q8, k8, v8, descale, scale, rows=None, *, quantise=True,
+                  norm_from_p8=False, lse_from_p8=False, shift=True, v_descale=True):
+    """oracle.attention_fp8 rewritten with switches for the planted slips."""
+    q = DEC(q8) * float(descale[0])
+    k = DEC(k8) * float(descale[1])
+    v = DEC(v8) * (float(descale[2]) if v_descale else 1.0)
+    if rows is not None:
+        q = q[:, :, np.asarray(rows)]
+    s = float(scale) * (q @ np.swapaxes(k, -1, -2))
+    m = s.max(axis=-1, keepdims=True) if shift else np.zeros_like(s[..., :1])
+    p = np.exp(s - m)
+    p8 = RND(448.0 * p) if quantise else 448.0 * p
+    l = (p8 / 448.0 if norm_from_p8 else p).sum(axis=-1, keepdims=True)
+    o = (p8 @ v) / (448.0 * l)
+    lse_l = (p8 / 448.0 if lse_from_p8 else p).sum(axis=-1)
+    return o, m[..., 0] + np.log(lse_l)
+
+
+def g_p_not_quantised(*a, **kw):
+    return _p8_attention(*a, quantise=False, **kw)
+
+
+def g_normaliser_from_rounded_p(*a, **kw):
+    return _p8_attention(*a, norm_from_p8=True, **kw)
+
+
+def g_lse_from_rounded_p(*a, **kw):
+    return _p8_attention(*a, lse_from_p8=True, **kw)
+
+
+def g_no_max_shift(*a, **kw):
+    return _p8_attention(*a, shift=False, **kw)
+
+
+def g_v_descale_dropped(*a, **kw):
+    return _p8_attention(*a, v_descale=False, **kw)
+
+
 # ---- which pins cover which function ---------------------------------------
 
 ATTN_PINS = [
@@ -395,6 +436,15 @@ ROWS_PINS = [
     lambda: pins.test_rows_v_exact_power_of_two_probabilities(64),
 ]
 
+FP8_ATTN_PINS = [
+    pins.test_fp8_attention_identical_keys_exact,
+    pins.test_fp8_attention_normalises_by_the_unrounded_probabilities,
+    pins.test_fp8_attention_exact_power_of_two_probabilities,
+    pins.test_fp8_attention_close_to_dequantised_attention,
+    lambda: fp8_bound.test_oracle_x448_rounding_is_within_its_bound(1.0),
+    lambda: fp8_bound.test_oracle_x448_rounding_is_within_its_bound(4.0),
+]
+
 # (name patched in ``oracle`` -- or in ``oracle.layout`` / ``oracle.residual``
 # for a dotted name -- and, where the oracle calls it internally, in
 # ``oracle.fp8``; the mutant; the pins that cover it)
@@ -449,6 +499,14 @@ MUTANTS = {
                                              ROWS_PINS),
     "rows: P block exponent from the block minimum": ("p_block_exponents",
                                                       p_blocks_take_the_min, ROWS_PINS),
+    "fp8 attention: P not quantised": ("attention_fp8", g_p_not_quantised, FP8_ATTN_PINS),
+    "fp8 attention: normaliser from the rounded P": ("attention_fp8",
+                                                     g_normaliser_from_rounded_p, FP8_ATTN_PINS),
+    "fp8 attention: LSE from the rounded P": ("attention_fp8", g_lse_from_rounded_p,
+                                              FP8_ATTN_PINS),
+    "fp8 attention: no max shift before rounding": ("attention_fp8", g_no_max_shift,
+                                                    FP8_ATTN_PINS),
+    "fp8 attention: V descale dropped": ("attention_fp8", g_v_descale_dropped, FP8_ATTN_PINS),
 }
 
 
@@ -478,9 +536,9 @@ def _patch(monkeypatch, name, fn):
 
 
 @pytest.mark.parametrize("pin_list", [ATTN_PINS, MERGE_PINS, RESID_PINS, FP8_PINS, LAYOUT_PINS,
-                                      FBCACHE_PINS, ROWS_PINS],
+                                      FBCACHE_PINS, ROWS_PINS, FP8_ATTN_PINS],
                          ids=["attention", "merge", "residual", "fp8", "layout", "fbcache",
-                              "rows"])
+                              "rows", "fp8 attention"])
 def test_pins_pass_on_the_real_oracle(pin_list):
     assert _failures(pin_list) == 0
 

@@ -409,6 +409,21 @@ def test_fp8_attention_exact_power_of_two_probabilities():
     assert lse[0, 0, 0] == pytest.approx(math.log(p.sum()), rel=1e-14)
 
 
+def test_fp8_attention_normalises_by_the_unrounded_probabilities():
+    # Two keys with logits 0 and -ln(448/300): p = 1 and 300/448, so
+    # 448 p = 448 (exact) and 300, which E4M3 rounds to 288 (spacing 32
+    # above 256, the midpoint 304). With V = 1 for both keys the rounded
+    # weights sum to 736 while the normaliser l = 1 + 300/448 comes from the
+    # unrounded p: O = 736 / (448 l) = 736/748, not 1.
+    scale = math.log(448.0 / 300.0)
+    q8 = oracle.e4m3_encode(np.ones((1, 1, 1, 1)))
+    k8 = oracle.e4m3_encode(np.array([0.0, -1.0]).reshape(1, 1, 2, 1))
+    v8 = oracle.e4m3_encode(np.ones((1, 1, 2, 1)))
+    o, lse = oracle.attention_fp8(q8, k8, v8, (1.0, 1.0, 1.0), scale)
+    assert o[0, 0, 0, 0] == pytest.approx(736.0 / 748.0, rel=1e-12)
+    assert lse[0, 0, 0] == pytest.approx(math.log(1.0 + 300.0 / 448.0), rel=1e-14)
+
+
 def test_fp8_attention_close_to_dequantised_attention():
     # Only P is rounded beyond the dequantised inputs: each 448 p is within
     # 2^-4 relative (normal range) or 2^-10 absolute (subnormal range).
