@@ -61,6 +61,45 @@ def test_attention_keys_past_2_31_elements():
             assert abs(float(lse[0, h, r]) - math.log(l_exact)) < 1e-4, (h, r, float(lse[0, h, r]))
 
 
+def test_fp8_attention_keys_past_2_31_bytes():
+    """The per-tensor fp8 kernel on the same construction as above, in E4M3
+    codes (descales 1): K/V of two heads of 2^24 + 37 keys are 2.15e9 bytes
+    each, all zero but the last key (k = 1, v = c_h); q = (192, 0, ...),
+    0 or (-192, 0, ...). Only the last key carries a value, so O has no
+    accumulation error: O = c_h w with w = e^s/(e^s + N - 1) up to the E4M3
+    rounding of the kernel's 108 p (2^-4 relative, or 2^-10/(108 l) of |c_h|
+    below E4M3's normal range, l the exact normaliser against the row max)
+    and two bf16 roundings; LSE comes from the unrounded p."""
+    H, N, D = 2, (1 << 24) + 37, 128
+    assert N * D > TWO31
+    _case("attn_fwd_fp8 large", H=H, Nkv=N, D=D)
+    code = lambda x: int(torch.tensor([x]).to(torch.float8_e4m3fn).view(torch.uint8))  # noqa: E731
+    scale = D ** -0.5
+    k8 = torch.zeros((1, H, N, D), dtype=torch.uint8, device=DEV)
+    v8 = torch.zeros_like(k8)
+    k8[0, :, N - 1, 0] = code(1.0)
+    c = [2.0, -3.0]
+    for h in range(H):
+        v8[0, h, N - 1, :] = code(c[h])
+    q8 = torch.zeros((1, H, 3, D), dtype=torch.uint8, device=DEV)
+    q8[0, :, 0, 0] = code(192.0)
+    q8[0, :, 2, 0] = code(-192.0)
+    ds = torch.ones(3, dtype=torch.float32, device=DEV)
+    o, lse = dta.attn_fwd_fp8(q8, k8, v8, ds, scale)
+    torch.cuda.synchronize()
+    del k8, v8
+    _free()
+    for h in range(H):
+        for r, s in ((0, scale * 192.0), (1, 0.0), (2, -scale * 192.0)):
+            m = max(s, 0.0)
+            l = math.exp(s - m) + (N - 1) * math.exp(-m)
+            o_exact = c[h] * math.exp(s - m) / l
+            bound = (2 ** -4 + 2 ** -8) * abs(o_exact) + 2 ** -10 * abs(c[h]) / (108.0 * l) + 1e-30
+            got = o[0, h, r].double().cpu()
+            assert float((got - o_exact).abs().max()) <= bound, (h, r, got[:4], o_exact, bound)
+            assert abs(float(lse[0, h, r]) - (m + math.log(l))) < 1e-4, (h, r, float(lse[0, h, r]))
+
+
 def test_merge_rows_past_2_31_elements():
     """Two partials of 2^23 + 5 rows x 128 (2.15e9 elements together): O_0 = 1,
     O_1 = 3, LSE_0 = 0, LSE_1 = ln 3, so O = (1 + 3*3) / 4 = 2.5 and
