@@ -1,7 +1,9 @@
 """include/dta.h is a C header and libdta.so a C library: a C11 program
 built with gcc against them links, and every argument check it calls returns
-its documented status before any HIP call (runs without a GPU)."""
+its documented status before any HIP call (runs without a GPU). The same
+holds for the library built by the package's CMakeLists.txt."""
 
+import ctypes
 import os
 import shutil
 import subprocess
@@ -53,20 +55,51 @@ int main(void) {
 """
 
 
-def test_a_c_program_builds_against_the_header_and_library(tmp_path):
+def _consumer(tmp_path, lib_dir):
+    """Builds the C program against dta.h and lib_dir/libdta.so and runs it."""
     gcc = shutil.which("gcc")
     if gcc is None:
         pytest.skip("gcc not available")
-    if not os.path.exists(_lib.LIB_PATH):
-        pytest.fail("libdta.so is not built")
     src = tmp_path / "consumer.c"
     src.write_text(C_SOURCE)
     exe = tmp_path / "consumer"
     build = subprocess.run(
         [gcc, "-std=c11", "-Wall", "-Werror", "-D__HIP_PLATFORM_AMD__",
          "-I", os.path.join(ROOT, "include"), "-I", "/opt/rocm/include", str(src),
-         "-L", PKG, "-ldta", "-Wl,-rpath," + PKG, "-o", str(exe)],
+         "-L", lib_dir, "-ldta", "-Wl,-rpath," + lib_dir, "-o", str(exe)],
         capture_output=True, text=True)
     assert build.returncode == 0, build.stderr
     run = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
     assert run.returncode == 0 and run.stdout.strip() == "ok", run.stdout + run.stderr
+
+
+def test_a_c_program_builds_against_the_header_and_library(tmp_path):
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libdta.so is not built")
+    _consumer(tmp_path, PKG)
+
+
+def test_the_cmake_build_gives_the_same_c_library(tmp_path):
+    """The package's CMakeLists.txt builds libdta.so for gfx950 with the same
+    device flags as build.py; it exports every function include/dta.h
+    declares, and the C program above runs against it."""
+    cmake, ninja = shutil.which("cmake"), shutil.which("ninja")
+    if cmake is None or ninja is None:
+        pytest.skip("cmake or ninja not available")
+    bdir = tmp_path / "build"
+    cfg = subprocess.run([cmake, "-S", os.path.join(ROOT, "diffusion_transformer_attention_flash_amd"),
+                          "-B", str(bdir), "-G", "Ninja"], capture_output=True, text=True)
+    assert cfg.returncode == 0, cfg.stdout + cfg.stderr
+    flags = (bdir / "build.ninja").read_text()
+    assert "--offload-arch=gfx950" in flags and "--offload-arch=gfx9" not in flags.replace(
+        "--offload-arch=gfx950", "")
+    assert "-Xclang -target-feature -Xclang -packed-fp32-ops" in flags
+    bld = subprocess.run([cmake, "--build", str(bdir), "-j", "6"], capture_output=True, text=True)
+    assert bld.returncode == 0, bld.stdout[-4000:] + bld.stderr[-4000:]
+    so = bdir / "libdta.so"
+    lib = ctypes.CDLL(str(so))
+    for name in _lib.SIGNATURES:
+        assert hasattr(lib, name), name
+    lib.dta_ws_bytes.restype = ctypes.c_size_t
+    assert lib.dta_ws_bytes() == _lib.lib().dta_ws_bytes()
+    _consumer(tmp_path, str(bdir))
