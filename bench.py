@@ -28,6 +28,16 @@ a cold read-only scan and a device copy of the same bytes (``cold``).
 the mean of the same per-launch events. ``cpu_baseline`` times the float64
 CPU oracle on bounded samples of the five configurations.
 
+``shares`` times one GPU's share of the HunyuanVideo attention when it is
+spread over 8 GPUs, at that share's real shape (no collective runs; the
+exchanged buffers are built in place):
+  * ulysses_8: 3 of the 24 heads over all 119 056 tokens. The received
+    token shards are joined (seq_concat of Q, K and V), attn_fwd runs, and
+    O is cut back into token shards (seq_split) for the return exchange.
+  * ring_8: one rank's 14 882 query rows of all 24 heads against the 8 K/V
+    shards in turn: attn_fwd on the first, attn_fwd_accum on the other 7.
+Both do 1/8 of the video FLOPs.
+
 Prints ONE JSON line.
 """
 
@@ -329,6 +339,94 @@ def cpu_baseline(dev, scale):
     }
 
 
+def share_runs(qv, kv, vv, scale, reps, n_gpus=8):
+    """One GPU's share of the attention on qv/kv/vv [1, H, N, D] spread over
+    n_gpus GPUs, Ulysses (heads) and ring (query rows, K/V shards); see the
+    module docstring. Returns timings in ms and rates."""
+    import torch
+    import diffusion_transformer_attention_flash_amd as dta
+    B, H, N, D = qv.shape
+    assert B == 1 and H % n_gpus == 0 and N % n_gpus == 0
+    hs, n = H // n_gpus, N // n_gpus
+    lens = [n] * n_gpus
+    Ev = lambda: torch.cuda.Event(enable_timing=True)
+    flop = attn_flop(1, H, N, N, D) / n_gpus
+
+    def timed(fn, marks):
+        fn()
+        torch.cuda.synchronize()
+        runs = []
+        for _ in range(reps):
+            ev = [Ev() for _ in range(marks + 1)]
+            ev[0].record()
+            fn(ev)
+            runs.append(ev)
+        torch.cuda.synchronize()
+        return [[e[i].elapsed_time(e[i + 1]) for i in range(marks)] for e in runs]
+
+    # Ulysses: the receive buffers of the all-to-all hold this GPU's heads of
+    # every token shard, packed shard after shard.
+    recv = [torch.cat([t[:, :hs, r * n:(r + 1) * n].reshape(-1) for r in range(n_gpus)])
+            for t in (qv, kv, vv)]
+    qkv = [torch.empty((1, hs, N, D), dtype=qv.dtype, device=qv.device) for _ in range(3)]
+    o = torch.empty_like(qkv[0])
+    lse = torch.empty((1, hs, N), dtype=torch.float32, device=qv.device)
+    send = torch.empty(hs * N * D, dtype=qv.dtype, device=qv.device)
+
+    def ulysses(ev=None):
+        for src, dst in zip(recv, qkv):
+            dta.seq_concat(src, lens, 1, hs, D, out=dst)
+        if ev:
+            ev[1].record()
+        dta.attn_fwd(qkv[0], qkv[1], qkv[2], scale, o=o, lse=lse)
+        if ev:
+            ev[2].record()
+        dta.seq_split(o, lens, parts=send)
+        if ev:
+            ev[3].record()
+
+    t = timed(ulysses, 3)
+    att = stats_ms([x[1] for x in t])
+    uly = {"shape": "B=1, H=%d of %d, N=%d, D=%d" % (hs, H, N, D),
+           "attn_fwd": {**att, "TFLOP/s_median": flop / (att["median_ms"] * 1e-3) / 1e12,
+                        "frac_bf16_peak": flop / (att["median_ms"] * 1e-3) / 1e12
+                        / PEAK_BF16_TFLOPS},
+           "seq_concat_qkv_ms_median": statistics.median(x[0] for x in t),
+           "seq_split_o_ms_median": statistics.median(x[2] for x in t),
+           "total_ms_median": statistics.median(sum(x) for x in t),
+           "layout_bytes": 2 * 4 * hs * N * D * 2}
+    del recv, qkv, o, lse, send
+
+    # Ring: rank 0's query rows; the K/V shards arrive in turn.
+    qr = qv[:, :, :n].contiguous()
+    ks = [kv[:, :, r * n:(r + 1) * n].contiguous() for r in range(n_gpus)]
+    vs = [vv[:, :, r * n:(r + 1) * n].contiguous() for r in range(n_gpus)]
+    o = torch.empty_like(qr)
+    lse = torch.empty((1, H, n), dtype=torch.float32, device=qv.device)
+
+    def ring(ev=None):
+        dta.attn_fwd(qr, ks[0], vs[0], scale, o=o, lse=lse)
+        if ev:
+            ev[1].record()
+        for r in range(1, n_gpus):
+            dta.attn_fwd_accum(qr, ks[r], vs[r], o, lse, scale)
+            if ev:
+                ev[r + 1].record()
+
+    t = timed(ring, n_gpus)
+    tot = stats_ms([sum(x) for x in t])
+    step_flop = flop / n_gpus
+    rng = {"shape": "B=1, H=%d, Nq=%d per rank, %d K/V shards of %d, D=%d" % (H, n, n_gpus, n, D),
+           **tot, "TFLOP/s_median": flop / (tot["median_ms"] * 1e-3) / 1e12,
+           "frac_bf16_peak": flop / (tot["median_ms"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+           "first_step_attn_fwd_ms_median": statistics.median(x[0] for x in t),
+           "accum_step_ms_median": statistics.median(v for x in t for v in x[1:]),
+           "step_TFLOP/s_median": step_flop / (statistics.median(v for x in t for v in x[1:])
+                                               * 1e-3) / 1e12}
+    del qr, ks, vs, o, lse
+    return {"n_gpus": n_gpus, "flop_per_gpu": flop, "ulysses_8": uly, "ring_8": rng}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -337,6 +435,8 @@ def main():
     ap.add_argument("--video-reps", type=int, default=5)
     ap.add_argument("--no-video", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-shares", action="store_true",
+                    help="skip the one-GPU shares of the 8-GPU video layouts")
     ap.add_argument("--legs", default="all",
                     help="comma-separated subset of attn,chunks,merge,quant,fp8,residual "
                          "(profiling runs only; the step needs all)")
@@ -572,6 +672,7 @@ def main():
     # the engine clock is sampled while the bf16 launches run.
     cus, max_mhz = rocminfo_gpu()
     video = None
+    shares = None
     load_mhz = None
     if not args.no_video:
         cv = workloads.CONFIGS["hunyuan_720p_129f"]
@@ -598,6 +699,11 @@ def main():
                              "video tokens), D=128, bf16 attn_fwd",
                  **st, **tf(fv, st),
                  "frac_bf16_peak": fv / (st["median_ms"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+        if not args.no_shares:
+            del ov, lv
+            shares = share_runs(qv, kv, vv, sv, reps)
+            ov = torch.empty_like(qv)
+            lv = torch.empty((cv["B"], cv["H"], cv["N"]), dtype=torch.float32, device=dev)
         (q8v, k8v, v8v), dsv = dta.fp8_quant_per_tensor_multi([qv, kv, vv])
         del qv, kv, vv
         dta.attn_fwd_fp8(q8v, k8v, v8v, dsv, sv, o=ov, lse=lv)
@@ -688,6 +794,7 @@ def main():
         "cold": cold,
         "ring_fused_8_steps": ring,
         "video": video,
+        "shares": shares,
         "wall_s_timed": wall,
     }
     print(json.dumps(out))
