@@ -40,3 +40,24 @@ def test_bench_prints_one_json_line():
     assert 0 < rf["frac"] < 1 and abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-9
     assert "traffic" in rf and "achieved" in rf
     assert "workload" in d["config"]
+
+
+@pytest.mark.gpu
+def test_share_runs_small():
+    """bench.share_runs on a small tensor (8 heads, 1024 tokens over 8
+    GPUs): one head per GPU for Ulysses, 128 query rows per ring rank."""
+    import torch
+    sys.path.insert(0, ROOT)
+    import bench
+    import workloads
+    print("CASE bench.share_runs B=1 H=8 N=1024 D=128", flush=True)
+    q, k, v = workloads.make_qkv(7, 1, 8, 1024, 1024, 128, device="cuda")
+    s = bench.share_runs(q, k, v, 128 ** -0.5, reps=2, n_gpus=8)
+    assert s["n_gpus"] == 8 and s["flop_per_gpu"] == 4.0 * 8 * 1024 * 1024 * 128 / 8
+    u, r = s["ulysses_8"], s["ring_8"]
+    assert u["shape"] == "B=1, H=1 of 8, N=1024, D=128"
+    assert u["attn_fwd"]["reps"] == 2 and u["attn_fwd"]["median_ms"] > 0
+    assert u["seq_concat_qkv_ms_median"] > 0 and u["seq_split_o_ms_median"] > 0
+    assert u["layout_bytes"] == 2 * 4 * 1 * 1024 * 128 * 2
+    assert r["reps"] == 2 and r["median_ms"] > 0 and r["accum_step_ms_median"] > 0
+    assert 0 < r["frac_bf16_peak"] < 1 and 0 < u["attn_fwd"]["frac_bf16_peak"] < 1
