@@ -436,7 +436,8 @@ def main():
     ap.add_argument("--no-video", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-shares", action="store_true",
-                    help="skip the one-GPU shares of the 8-GPU video layouts")
+                    help="skip the one-GPU shares of the 8-GPU video layouts "
+                         "(built from the video tensors: --no-video skips them too)")
     ap.add_argument("--legs", default="all",
                     help="comma-separated subset of attn,chunks,merge,quant,fp8,residual "
                          "(profiling runs only; the step needs all)")
